@@ -1,0 +1,180 @@
+"""Throughput of the fused denoising step on one MI355X.
+
+One "step" is one pass of the whole hot path (vocabulary projection,
+temperature, entropy, Gumbel-max sampling, entropy-bounded commit and
+re-noise) over one batch of canvases.  Inputs are seeded synthetic tensors
+resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma_vocab]
+                    [--no-cpu-baseline] [--profile-only]
+
+Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the fused
+projection), timed with HIP events on the library's stream in a separate
+instrumented pass; ``cpu_baseline`` times the CPU oracle on a bounded sample
+of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("denoising steps/s and logit-elems/s (canvas·V) at canvas 256, V 262144; "
+          "% roofline")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, W, Hs):
+    """Time the oracle (as it stands) on one full step of the workload."""
+    from oracle import dgd_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = len(os.sched_getaffinity(0))
+    P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,
+                 stability_threshold=wl.stability_threshold, freeze=wl.freeze,
+                 final_emit=wl.final_emit)
+    steps = 5
+    t0 = time.perf_counter()
+    for c in range(wl.B):
+        st = O.init_block(O.new_state(wl.G, wl.L), 0, wl.L, wl.V, wl.seeds[c])
+        for s in range(steps):
+            st, _ = O.step(st, Hs[0, s, c], W, 0, s, P, wl.seeds[c], wl.bounds[c])
+    dt = time.perf_counter() - t0
+    return {
+        "value": steps / dt,
+        "unit": "steps/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{steps} denoising step(s) of {wl.name} ({wl.B}x{wl.L} positions x V={wl.V}, "
+                  f"d={wl.d}); oracle float64 numpy, projection via BLAS",
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=480)
+    ap.add_argument("--warmup", type=int, default=48)
+    ap.add_argument("--workload", default="gemma_vocab")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-only", action="store_true",
+                    help="only the timed loop (for rocprofv3 runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the denoising step of "
+              "this library is a single-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from uniform_state_discrete_step_amd import dgd
+    from uniform_state_discrete_step_amd.inputs import WORKLOADS, make_workload_arrays
+
+    wl = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    W, Hs = make_workload_arrays(wl, threads=16)
+    log(f"[bench] generated {wl.name} inputs in {time.perf_counter() - t0:.1f}s")
+    Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+    Hd = torch.from_numpy(Hs.view(np.int16)).to(dev)
+    ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev, outputs=False)
+    params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence, wl.stability_threshold,
+                             wl.freeze, wl.final_emit)
+    canvas = torch.zeros(wl.B * wl.G, dtype=torch.int32, device=dev)
+    committed = torch.zeros(wl.B * wl.G, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    blocks, N = wl.blocks, wl.N
+
+    def run_steps(k, start=0):
+        """Enqueue k consecutive denoising steps (block starts included)."""
+        for i in range(start, start + k):
+            g = i % (blocks * N)
+            b, s = divmod(g, N)
+            if s == 0:
+                dgd.dgd_init_block(canvas, committed, b, params, wl.seeds, ctx)
+            dgd.dgd_step(Hd[b, s].reshape(-1), Wd, canvas, committed, b, s, params, wl.seeds, ctx)
+
+    log(f"[bench] warmup {args.warmup} steps")
+    run_steps(args.warmup)
+    torch.cuda.synchronize()
+    start_ev = torch.cuda.Event(enable_timing=True)
+    stop_ev = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start_ev.record()
+    run_steps(args.steps, start=args.warmup)
+    stop_ev.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = start_ev.elapsed_time(stop_ev)
+    log(f"[bench] timed {args.steps} steps: {ms:.2f} ms (wall {wall * 1e3:.2f} ms)")
+    if args.profile_only:
+        return
+
+    # instrumented pass: HIP events around every fused-projection launch
+    ctx.time_k1 = True
+    dgd.dgd_run(Hd.reshape(-1), Wd, canvas, committed, params, wl.seeds, ctx)
+    k1_ms, k1_n = ctx.k1_time()
+    ctx.time_k1 = False
+    k1_avg_s = k1_ms / max(k1_n, 1) * 1e-3
+    M = wl.B * wl.L
+    alg_bytes = wl.V * wl.d * 2 + M * wl.d * 2
+    flops = 2.0 * M * wl.V * wl.d
+    gbs = alg_bytes / k1_avg_s / 1e9
+    tflops = flops / k1_avg_s / 1e12
+    hbm_frac = gbs / HBM_PEAK_GBS
+    mfma_frac = tflops / MFMA_BF16_PEAK_TFLOPS
+    bound = "hbm" if alg_bytes / (HBM_PEAK_GBS * 1e9) >= flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) else "mfma"
+    roof = ({"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+             "frac": hbm_frac} if bound == "hbm" else
+            {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+             "frac": mfma_frac})
+    roof.update({"traffic": None, "kernel": "k_project", "kernel_avg_us": k1_avg_s * 1e6,
+                 "kernel_launches": k1_n, "algorithmic_bytes_per_launch": alg_bytes,
+                 "flops_per_launch": flops,
+                 "other": {"hbm_GBs": gbs, "hbm_frac": hbm_frac, "mfma_TFLOPs": tflops,
+                           "mfma_frac": mfma_frac}})
+
+    steps_per_s = args.steps / (ms * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": steps_per_s,
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "canvases": wl.B, "canvas_len": wl.L, "vocab": wl.V,
+                   "hidden": wl.d, "gen_length": wl.G, "num_inference_steps": wl.N},
+        "logit_elems_per_s": steps_per_s * M * wl.V,
+        "step_frac_of_hbm_floor": (steps_per_s * alg_bytes) / (HBM_PEAK_GBS * 1e9),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on one step")
+        out["cpu_baseline"] = cpu_baseline(wl, W, Hs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * dgd.h - C ABI of the MI355X (gfx950) denoising-step library (libdgd.so).
+ *
+ * The library performs the per-step update of uniform-state discrete
+ * diffusion in the style of DiffusionGemma, as described by four pages:
+ *   - the ComfyUI node page "DiffusionGemma Denoise (KV Cache)", Inputs table
+ *     (knob names, units, defaults, the temperature schedule, block length);
+ *   - the ComfyUI-DiffusionGemma pack README, sections "What it is" (lowest
+ *     entropy positions freeze, the rest are re-noised) and "Terms and units";
+ *   - the TensorSharp DiffusionGemma model doc, section "3. Sampler contract"
+ *     (MaxDenoisingSteps, TMin/TMax, EntropyBound, StabilityThreshold,
+ *     ConfidenceThreshold, Seed);
+ *   - "The Annotated DiffusionGemma" walkthrough, section "Sampling" (apply
+ *     temperature, compute entropy, keep a low-entropy prefix and renoise the
+ *     rest, check for early stopping) and "Denoise, stage, commit, and
+ *     generate".
+ *
+ * One step of one canvas (block b, step s, N steps per block, gstep = b*N+s):
+ *   T_s   = t_max + (s/N)(t_min - t_max)                  (walkthrough, "Apply temperature")
+ *   z     = H W_vocab^T, bf16 inputs, fp32 accumulation   (tied unembedding)
+ *   x     = z / T_s
+ *   H_p   = -sum_v p_v ln p_v, p = softmax(x)             (nats; "Compute entropy")
+ *   a_p   = argmax_v x_v (first index on ties)
+ *   tok_p = argmax_v (x_v + g_v), g = -ln(-ln u), u from Philox4x32-10
+ *           word (v&3) of counter (v>>2, p_abs, gstep, 0), key = seed,
+ *           u = ((w >> 9) + 1/2) 2^-23                       (Gumbel-max sample)
+ *   converged = mean_p H_p < confidence AND argmax unchanged for
+ *               stability_threshold steps (argmax before step 0 = all 0)
+ *   final = converged OR s == N-1: every open position takes tok_p (or a_p
+ *           when final_emit), all positions end committed, the canvas is done.
+ *   otherwise: rank open positions by (H_p, p); rank r is accepted when the
+ *           float64 sum of the entropies ranked before it is <= entropy_bound
+ *           ("Keep a low-entropy prefix"); accepted positions take tok_p and
+ *           become committed; the other ranked positions are re-noised to
+ *           (w * V) >> 32 with w = Philox word 0 of (0, p_abs, gstep, 1).
+ *   A block starts from tokens (w * V) >> 32, w = Philox word 0 of
+ *   (0, p_abs, b, 2), with every position open.
+ *
+ * Memory.  Every device buffer is owned by the caller; the library allocates
+ * no device memory.  Pointers marked "device" must be device memory of the
+ * current HIP device; pointers marked "host" are read during the call only.
+ * Layouts are row-major and densely packed.  bf16 values are IEEE bfloat16
+ * bit patterns.
+ *
+ * Streams.  Work is enqueued on ctx->stream (a hipStream_t; NULL = the null
+ * stream) and the call returns without synchronising, unless ctx->k1_ms asks
+ * for kernel timing.  Outputs are valid once the stream has reached them.
+ * Calls that share a workspace or state buffer must be ordered on one stream.
+ *
+ * Errors.  Every entry point returns DGD_OK (0) or a negative code and never
+ * throws; dgd_last_error() describes the last failure of the calling thread.
+ * Invalid arguments are refused, never adjusted.  Argument checks happen on
+ * the host before any work is enqueued, so a refused call leaves every
+ * buffer untouched.
+ */
+#ifndef DGD_H
+#define DGD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DGD_OK            0
+#define DGD_EINVAL       (-1)  /* null pointer, knob out of range, bad shape           */
+#define DGD_EUNSUPPORTED (-2)  /* shape outside the limits below                        */
+#define DGD_EWORKSPACE   (-3)  /* workspace smaller than dgd_workspace_bytes()          */
+#define DGD_EHIP         (-4)  /* a HIP runtime call or kernel launch failed             */
+
+#define DGD_MAX_CANVASES   64     /* B  <= 64                                           */
+#define DGD_MAX_CANVAS_LEN 4096   /* L  <= 4096                                         */
+#define DGD_MAX_GEN_LENGTH 8192   /* G  <= 8192 (node page, gen_length row range)        */
+#define DGD_MAX_STEPS      1024   /* N  <= 1024 (node page, num_inference_steps range)   */
+#define DGD_MAX_VOCAB      (1 << 24)
+#define DGD_MAX_HIDDEN     65536
+
+typedef uint16_t dgd_bf16;
+
+/* Sampler knobs (node page "Inputs"; TensorSharp doc "3. Sampler contract").
+ * Ranges are checked on every call:
+ *   num_inference_steps  N in [1, 1024]
+ *   t_min, t_max         finite, in [0, 1], and every T_s > 0
+ *   confidence           early-stop mean-entropy threshold in nats, [0, 1]
+ *   stability_threshold  consecutive unchanged-argmax steps needed, [0, 1024]
+ *   freeze               1: committed positions stay frozen (default);
+ *                        0: every position is re-ranked each step
+ *   final_emit           0: the last step writes samples (default);
+ *                        1: it writes the argmax canvas                       */
+typedef struct dgd_params {
+  int32_t num_inference_steps;
+  float   t_min;
+  float   t_max;
+  float   confidence;
+  int32_t stability_threshold;
+  int32_t freeze;
+  int32_t final_emit;
+} dgd_params;
+
+/* Shapes, per-canvas knobs, scratch and optional outputs.
+ *   B  canvases denoised together, [1, 64]
+ *   L  canvas (block) length, [1, 4096]
+ *   V  vocabulary size, [1, 2^24]
+ *   d  hidden size, [8, 65536], a multiple of 8
+ *   G  generated length per canvas, a multiple of L, G <= 8192
+ *   entropy_bound  host float[B], nats, each in [0, 1]
+ *   workspace      device, at least dgd_workspace_bytes(B, L, V, d) bytes,
+ *                  256-byte aligned; contents need no initialisation
+ *   state          device, dgd_state_bytes(B, L) bytes, layout below;
+ *                  dgd_init_block() initialises it for a block
+ *   stream         hipStream_t
+ * Optional device outputs of dgd_step (NULL = not written), all for the step
+ * just taken, row index r = c*L + p:
+ *   entropy     float[B*L]   H_p in nats
+ *   argmax      int32[B*L]   a_p
+ *   token       int32[B*L]   tok_p (the Gumbel-max sample)
+ *   gap         float[B*L]   top-two gap of the Gumbel-perturbed tempered logits, nats
+ *   logits      float[B*L*V] z (fp32 accumulator, before temperature); validation only
+ *   commit_step int16[B*G]   step index s at which the position was last committed
+ *                            (untouched elsewhere; callers pre-fill, e.g. with -1)
+ * Optional host outputs (timing): when k1_ms is not NULL the call records HIP
+ * events around every launch of the fused projection kernel, synchronises
+ * before returning, and writes the summed kernel time in ms to *k1_ms and the
+ * number of launches timed to *k1_launches (if not NULL).                     */
+typedef struct dgd_ctx {
+  int32_t B, L, V, d, G;
+  const float* entropy_bound;
+  void*   workspace;
+  size_t  workspace_bytes;
+  void*   state;
+  void*   stream;
+  float*   entropy;
+  int32_t* argmax;
+  int32_t* token;
+  float*   gap;
+  float*   logits;
+  int16_t* commit_step;
+  double*  k1_ms;
+  int32_t* k1_launches;
+} dgd_ctx;
+
+/* State layout (device, int32/float words, in this order):
+ *   int32 prev_argmax [B*L]  argmax canvas of the previous step of the block
+ *   int32 stable_count[B]    consecutive steps with an unchanged argmax canvas
+ *   int32 done        [B]    1 once the canvas has taken its final step
+ *   int32 steps_used  [B]    steps taken in the current block
+ *   int32 converged   [B]    1 if the block ended by the early-stop rule
+ *   int32 n_committed [B]    committed positions of the current block
+ *   float mean_entropy[B]    mean entropy of the last step, nats
+ *   int32 new_commits [B]    positions committed by the last step
+ * The step reads and writes it; callers may read it after a stream sync, and
+ * may overwrite it to resume from a saved state.                            */
+size_t dgd_state_bytes(int32_t B, int32_t L);
+
+/* Bytes of scratch the step needs (per-slice softmax/entropy/Gumbel partials
+ * and per-position results); 0 if the shape is unsupported. */
+size_t dgd_workspace_bytes(int32_t B, int32_t L, int32_t V, int32_t d);
+
+/* Start block `block` of every canvas: uniform initial tokens (Philox word 0
+ * of counter (0, p_abs, block, 2)) over positions [block*L, (block+1)*L),
+ * committed = 0 there, and a fresh state for the block.  Earlier and later
+ * positions are untouched.
+ *   canvas     device int32[B*G], committed device uint8[B*G]
+ *   seed       host uint64[B] (Philox key: low word, high word)            */
+int dgd_init_block(int32_t* canvas, uint8_t* committed, int32_t block,
+                   const dgd_params* params, const uint64_t* seed, const dgd_ctx* ctx);
+
+/* One denoising step (block `block`, step `step` in [0, N)) of every canvas
+ * that is not done.  H: device bf16[B*L*d], the final hidden states of the B
+ * canvases for this step (row r = c*L + p).  W_vocab: device bf16[V*d], the
+ * tied embedding table.  canvas/committed: device int32/uint8[B*G], updated
+ * in place.  seed: host uint64[B].  The [B*L x V] logits never reach HBM
+ * unless ctx->logits asks for them. */
+int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_t* committed,
+             int32_t block, int32_t step, const dgd_params* params, const uint64_t* seed,
+             const dgd_ctx* ctx);
+
+/* Whole generation: for every block b in [0, G/L): dgd_init_block, then up
+ * to N steps (steps after a canvas is done leave it untouched; nothing
+ * synchronises with the host).  H_steps: device bf16[(G/L)*N*B*L*d], laid
+ * out [block][step][canvas][position][hidden].  Per-step outputs of ctx, if
+ * set, hold the last step taken. */
+int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas,
+            uint8_t* committed, const dgd_params* params, const uint64_t* seed,
+            const dgd_ctx* ctx);
+
+/* Validation helper: for n 32-bit Philox words (device uint32[n]) write the
+ * Gumbel noise the fused step adds to its logits, in base-2 units:
+ * out[i] = -log2(-log2(u_i)) with u_i = ((w_i >> 9) + 1/2) 2^-23, so that the
+ * natural-unit noise is out[i]*ln 2 - ln(ln 2).  Device float[n] output. */
+int dgd_debug_gumbel(const uint32_t* words, float* out, int64_t n, void* stream);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* dgd_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGD_H */

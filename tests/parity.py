@@ -1,0 +1,264 @@
+"""Lockstep comparison of the HIP step with the CPU oracle, with tie bands.
+
+Sticky commits cascade (one flipped decision changes every later step), so
+the GPU is compared in lockstep: before every step it receives the oracle's
+state (canvas, committed mask, previous argmax, stability count, done flag)
+and that single step's outputs are compared.
+
+Agreement criteria (float tolerances are those the method's specification
+fixes for bf16 inputs with fp32 accumulation):
+* entropies within 1e-3 nats at every position;
+* argmax equal unless the oracle's top two tempered logits are within 1e-5;
+* sampled tokens equal unless the oracle's top two Gumbel-perturbed logits
+  are within 1e-4;
+* commit decisions equal unless the position is in the commit band: its
+  entropy is within 1e-5 nats of the last accepted or first rejected
+  entropy, or it is one of those two ranks and the running sum before it is
+  within 1e-5 of the bound;
+* the early-stop decision equal unless |mean entropy - confidence| < 1e-5 or
+  an argmax band event moved the stability test;
+* re-noised and initial tokens bit-exact (pure integer functions).
+Band events are counted, never hidden.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+from oracle import dgd_oracle as O
+
+TOL_ENTROPY = 1e-3
+BAND_ARGMAX = 1e-5
+BAND_SAMPLE = 1e-4
+BAND_COMMIT = 1e-5
+BAND_CONV = 1e-5
+TOL_LOGIT_REL = 2e-2
+
+
+@dataclasses.dataclass
+class Report:
+    steps: int = 0
+    positions: int = 0
+    max_entropy_err: float = 0.0
+    argmax_band: int = 0
+    sample_band: int = 0
+    commit_band: int = 0
+    conv_band: int = 0
+    renoised: int = 0
+    accepted: int = 0
+    failures: list = dataclasses.field(default_factory=list)
+
+    def fail(self, msg):
+        if len(self.failures) < 50:
+            self.failures.append(msg)
+
+    def summary(self) -> str:
+        return (f"steps={self.steps} positions={self.positions} max|dH|={self.max_entropy_err:.2e} "
+                f"bands: argmax={self.argmax_band} sample={self.sample_band} "
+                f"commit={self.commit_band} convergence={self.conv_band} "
+                f"accepted={self.accepted} renoised={self.renoised}")
+
+
+def commit_band_positions(info, bound) -> set:
+    """Positions whose commit decision may legitimately differ (see module doc)."""
+    order = info.get("order")
+    if not order:
+        return set()
+    h = info["stats"]["entropy"].astype(np.float64)
+    sums = info["sums"]
+    acc = info["accepted"]
+    k = int(sum(1 for p in order if acc[p]))          # accepted ranks 0..k-1
+    edges = [r for r in (k - 1, k) if 0 <= r < len(order)]
+    band = set()
+    for r, p in enumerate(order):
+        if any(abs(h[p] - h[order[e]]) <= BAND_COMMIT for e in edges):
+            band.add(p)
+        if r in edges and abs(sums[r] - bound) <= BAND_COMMIT:
+            band.add(p)
+    return band
+
+
+def compare_stats(rep: Report, tag: str, st: dict, H_gpu, A_gpu, T_gpu, rows=None):
+    """Entropy / argmax / token agreement for the rows of an oracle stats dict."""
+    H_o, A_o, T_o = st["entropy"], st["argmax"], st["token"]
+    err = float(np.max(np.abs(H_gpu.astype(np.float64) - H_o.astype(np.float64))))
+    rep.max_entropy_err = max(rep.max_entropy_err, err)
+    if err > TOL_ENTROPY:
+        rep.fail(f"{tag}: entropy error {err:.3e} > {TOL_ENTROPY}")
+    am = np.nonzero(A_gpu != A_o)[0]
+    for i in am:
+        if st["argmax_gap"][i] < BAND_ARGMAX:
+            rep.argmax_band += 1
+        else:
+            rep.fail(f"{tag}: argmax differs at row {i if rows is None else rows[i]} "
+                     f"(gpu {A_gpu[i]}, oracle {A_o[i]}, gap {st['argmax_gap'][i]:.3e})")
+    tm = np.nonzero(T_gpu != T_o)[0]
+    for i in tm:
+        if st["gap"][i] < BAND_SAMPLE:
+            rep.sample_band += 1
+        else:
+            rep.fail(f"{tag}: token differs at row {i if rows is None else rows[i]} "
+                     f"(gpu {T_gpu[i]}, oracle {T_o[i]}, gap {st['gap'][i]:.3e})")
+    return set(am.tolist()), set(tm.tolist())
+
+
+def compare_step(rep: Report, tag: str, before: O.CanvasState, after: O.CanvasState, info: dict,
+                 gpu: dict, L: int, V: int, block: int, step: int, params: O.Params, seed: int,
+                 bound: float):
+    """Compare one canvas' step.  ``gpu`` holds the GPU's outputs and new state."""
+    base = block * L
+    blk = slice(base, base + L)
+    if info.get("skipped"):
+        if not (np.array_equal(gpu["canvas"], before.canvas)
+                and np.array_equal(gpu["committed"], before.committed)):
+            rep.fail(f"{tag}: a done canvas was modified")
+        return
+    rep.steps += 1
+    rep.positions += L
+    st = info["stats"]
+    am_set, tok_set = compare_stats(rep, tag, st, gpu["entropy"], gpu["argmax"], gpu["token"])
+    if not np.array_equal(gpu["prev_argmax"], gpu["argmax"]):
+        rep.fail(f"{tag}: state prev_argmax is not this step's argmax")
+    # untouched regions
+    if not np.array_equal(np.delete(gpu["canvas"], np.arange(base, base + L)),
+                          np.delete(before.canvas, np.arange(base, base + L))):
+        rep.fail(f"{tag}: positions outside the block changed")
+
+    gpu_final = bool(gpu["done"])
+    if gpu_final != info["final"]:
+        near = abs(info["mean_H"] - float(np.float32(params.confidence))) < BAND_CONV
+        if near or am_set:
+            rep.conv_band += 1
+        else:
+            rep.fail(f"{tag}: final-step decision differs (gpu {gpu_final}, oracle "
+                     f"{info['final']}, mean H {info['mean_H']:.6g})")
+        return
+    if int(gpu["steps_used"]) != step + 1:
+        rep.fail(f"{tag}: steps_used {gpu['steps_used']} != {step + 1}")
+
+    g_can, g_com = gpu["canvas"][blk], gpu["committed"][blk]
+    o_can, o_com = after.canvas[blk], after.committed[blk]
+    b_can, b_com = before.canvas[blk], before.committed[blk]
+    if info["final"]:
+        if not np.all(g_com == 1):
+            rep.fail(f"{tag}: final step left positions open")
+        for p in range(L):
+            if g_can[p] != o_can[p]:
+                band = (p in am_set) if params.final_emit else (p in tok_set)
+                if not band:
+                    rep.fail(f"{tag}: final token differs at {p} (gpu {g_can[p]}, oracle {o_can[p]})")
+        return
+
+    band = commit_band_positions(info, bound)
+    p_abs = base + np.arange(L)
+    gstep = block * params.N + step
+    renoise = O.renoise_token(seed, p_abs, gstep, V)
+    for p in range(L):
+        if g_com[p] != o_com[p]:
+            if p in band:
+                rep.commit_band += 1
+            else:
+                rep.fail(f"{tag}: commit decision differs at {p} (gpu {g_com[p]}, oracle {o_com[p]},"
+                         f" H {st['entropy'][p]:.6g})")
+            continue
+        eligible = params.freeze == 0 or b_com[p] == 0
+        if not eligible:
+            if g_can[p] != b_can[p]:
+                rep.fail(f"{tag}: frozen position {p} changed")
+            continue
+        if g_com[p] == 1:
+            rep.accepted += 1
+            if g_can[p] != gpu["token"][p]:
+                rep.fail(f"{tag}: accepted position {p} does not hold its sample")
+            if g_can[p] != o_can[p] and p not in tok_set:
+                rep.fail(f"{tag}: accepted token differs at {p}")
+        else:
+            rep.renoised += 1
+            if g_can[p] != renoise[p] or o_can[p] != renoise[p]:
+                rep.fail(f"{tag}: re-noised token differs at {p} (gpu {g_can[p]}, "
+                         f"oracle {o_can[p]}, expected {renoise[p]})")
+
+
+class Lockstep:
+    """Drive the HIP library and the oracle side by side on one workload."""
+
+    def __init__(self, wl, W, Hs, device, logits=False):
+        import torch
+        from uniform_state_discrete_step_amd import dgd
+        self.dgd, self.torch = dgd, torch
+        self.wl, self.W, self.Hs, self.dev = wl, W, Hs, device
+        self.Wd = torch.from_numpy(W.view(np.int16)).to(device)
+        self.Hd = torch.from_numpy(Hs.view(np.int16)).to(device)
+        self.ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=device,
+                               logits=logits)
+        self.params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence,
+                                      wl.stability_threshold, wl.freeze, wl.final_emit)
+        self.P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,
+                          stability_threshold=wl.stability_threshold, freeze=wl.freeze,
+                          final_emit=wl.final_emit)
+        self.canvas = torch.zeros(wl.B * wl.G, dtype=torch.int32, device=device)
+        self.committed = torch.zeros(wl.B * wl.G, dtype=torch.uint8, device=device)
+        self.W64 = O.bf16_to_f64(W)
+        self.states = [O.new_state(wl.G, wl.L) for _ in range(wl.B)]
+
+    def push_state(self):
+        """Copy the oracle's state of every canvas into the GPU buffers."""
+        torch, wl = self.torch, self.wl
+        can = np.concatenate([s.canvas for s in self.states]).astype(np.int32)
+        com = np.concatenate([s.committed for s in self.states]).astype(np.uint8)
+        self.canvas.copy_(torch.from_numpy(can))
+        self.committed.copy_(torch.from_numpy(com))
+        sv = self.ctx.state_views()
+        sv["prev_argmax"].copy_(torch.from_numpy(
+            np.concatenate([s.prev_argmax for s in self.states]).astype(np.int32)))
+        sv["stable_count"].copy_(torch.tensor([s.stable_count for s in self.states], dtype=torch.int32))
+        sv["done"].copy_(torch.tensor([int(s.done) for s in self.states], dtype=torch.int32))
+        sv["steps_used"].copy_(torch.tensor([s.steps_used for s in self.states], dtype=torch.int32))
+
+    def pull(self, c):
+        wl = self.wl
+        sl = slice(c * wl.L, (c + 1) * wl.L)
+        sv = self.ctx.state_views()
+        return {
+            "entropy": self.ctx.entropy[sl].cpu().numpy(),
+            "argmax": self.ctx.argmax[sl].cpu().numpy().astype(np.int64),
+            "token": self.ctx.token[sl].cpu().numpy().astype(np.int64),
+            "gap": self.ctx.gap[sl].cpu().numpy(),
+            "canvas": self.canvas[c * wl.G:(c + 1) * wl.G].cpu().numpy().astype(np.int64),
+            "committed": self.committed[c * wl.G:(c + 1) * wl.G].cpu().numpy(),
+            "prev_argmax": sv["prev_argmax"][sl].cpu().numpy().astype(np.int64),
+            "done": int(sv["done"][c]),
+            "steps_used": int(sv["steps_used"][c]),
+        }
+
+    def run(self, blocks=None, steps=None, rep: Report = None, progress=None) -> Report:
+        torch, wl, dgd = self.torch, self.wl, self.dgd
+        rep = rep or Report()
+        for b in (range(wl.blocks) if blocks is None else blocks):
+            self.states = [O.init_block(s, b, wl.L, wl.V, wl.seeds[c])
+                           for c, s in enumerate(self.states)]
+            dgd.dgd_init_block(self.canvas, self.committed, b, self.params, wl.seeds, self.ctx)
+            torch.cuda.synchronize()
+            can = self.canvas.cpu().numpy()
+            for c, s in enumerate(self.states):
+                if not np.array_equal(can[c * wl.G:(c + 1) * wl.G], s.canvas):
+                    rep.fail(f"block {b} canvas {c}: initial tokens differ")
+            for s_idx in (range(wl.N) if steps is None else steps):
+                self.push_state()
+                dgd.dgd_step(self.Hd[b, s_idx].reshape(-1), self.Wd, self.canvas, self.committed,
+                             b, s_idx, self.params, wl.seeds, self.ctx)
+                torch.cuda.synchronize()
+                for c in range(wl.B):
+                    before = self.states[c]
+                    after, info = O.step(before, self.Hs[b, s_idx, c], self.W, b, s_idx, self.P,
+                                         wl.seeds[c], wl.bounds[c], W64=self.W64)
+                    compare_step(rep, f"block {b} step {s_idx} canvas {c}", before, after, info,
+                                 self.pull(c), wl.L, wl.V, b, s_idx, self.P, wl.seeds[c],
+                                 float(np.float32(wl.bounds[c])))
+                    self.states[c] = after
+                if progress:
+                    progress(b, s_idx, rep)
+                if all(s.done for s in self.states):
+                    break
+        return rep

@@ -1,0 +1,133 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library must load, export every function include/dgd.h declares, size
+its buffers as documented, and refuse invalid arguments on the host before
+any GPU work is enqueued (so these calls never touch a device).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from uniform_state_discrete_step_amd import dgd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "dgd.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dgd_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return dgd.load_library()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert set(names) == set(dgd.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_state_and_workspace_sizes(lib):
+    assert dgd.dgd_state_bytes(1, 256) == (256 + 7) * 4
+    assert dgd.dgd_state_bytes(8, 256) == (8 * 256 + 56) * 4
+    assert dgd.dgd_state_bytes(0, 16) == 0
+    # 256 positions x 512 vocabulary groups x 32-byte records dominate
+    ws = dgd.dgd_workspace_bytes(1, 256, 262144, 2816)
+    assert 256 * 512 * 32 <= ws <= 256 * 512 * 32 + 8192
+    assert dgd.dgd_workspace_bytes(1, 16, 1024, 64) >= 16 * 8 * 32
+    for bad in [(0, 16, 1024, 64), (65, 16, 1024, 64), (1, 4097, 1024, 64), (1, 16, 0, 64),
+                (1, 16, 1024, 60), (1, 16, 1024, 0), (1, 16, (1 << 24) + 1, 64)]:
+        assert dgd.dgd_workspace_bytes(*bad) == 0, bad
+
+
+FAKE = 0x10000  # never dereferenced: every call below is refused on the host
+
+
+def _ctx(**kw):
+    c = dgd.DgdCtx()
+    c.B, c.L, c.V, c.d, c.G = kw.get("B", 1), kw.get("L", 16), kw.get("V", 1024), kw.get("d", 64), kw.get("G", 16)
+    bounds = kw.get("bounds", [0.1] * c.B)
+    c._keep = (ctypes.c_float * len(bounds))(*bounds)
+    c.entropy_bound = c._keep if kw.get("with_bounds", True) else None
+    c.workspace = kw.get("workspace", FAKE * 16)
+    c.workspace_bytes = kw.get("workspace_bytes", 1 << 30)
+    c.state = kw.get("state", FAKE)
+    return c
+
+
+def _step(lib, ctx, params=None, seeds=(0,), block=0, step=0, H=FAKE, W=FAKE):
+    p = params or dgd.make_params(N=8)
+    s = (ctypes.c_uint64 * len(seeds))(*seeds)
+    return lib.dgd_step(H, W, FAKE, FAKE, block, step, ctypes.byref(p), s, ctypes.byref(ctx))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), dgd.DGD_EINVAL),
+    (dict(N=1025), dgd.DGD_EINVAL),
+    (dict(t_min=float("nan")), dgd.DGD_EINVAL),
+    (dict(t_max=1.5), dgd.DGD_EINVAL),
+    (dict(t_min=0.0, t_max=0.0), dgd.DGD_EINVAL),
+    (dict(confidence=-0.1), dgd.DGD_EINVAL),
+    (dict(stability_threshold=-1), dgd.DGD_EINVAL),
+    (dict(freeze=2), dgd.DGD_EINVAL),
+    (dict(final_emit=-1), dgd.DGD_EINVAL),
+])
+def test_invalid_knobs_are_refused(lib, kw, code):
+    args = dict(N=8)
+    args.update(kw)
+    assert _step(lib, _ctx(), params=dgd.make_params(**args)) == code
+    assert dgd.dgd_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=0), dgd.DGD_EUNSUPPORTED),
+    (dict(B=65, bounds=[0.1] * 65), dgd.DGD_EUNSUPPORTED),
+    (dict(L=0), dgd.DGD_EUNSUPPORTED),
+    (dict(L=5000, G=5000), dgd.DGD_EUNSUPPORTED),
+    (dict(G=24), dgd.DGD_EINVAL),
+    (dict(G=8 * 1024 + 16), dgd.DGD_EINVAL),
+    (dict(V=0), dgd.DGD_EUNSUPPORTED),
+    (dict(d=60), dgd.DGD_EUNSUPPORTED),
+    (dict(bounds=[1.5]), dgd.DGD_EINVAL),
+    (dict(bounds=[float("inf")]), dgd.DGD_EINVAL),
+    (dict(with_bounds=False), dgd.DGD_EINVAL),
+    (dict(state=None), dgd.DGD_EINVAL),
+    (dict(workspace=None), dgd.DGD_EINVAL),
+    (dict(workspace=FAKE * 16 + 8), dgd.DGD_EINVAL),
+    (dict(workspace_bytes=100), dgd.DGD_EWORKSPACE),
+])
+def test_invalid_shapes_and_buffers_are_refused(lib, kw, code):
+    assert _step(lib, _ctx(**kw)) == code
+
+
+def test_invalid_step_block_and_pointers_are_refused(lib):
+    assert _step(lib, _ctx(), step=8) == dgd.DGD_EINVAL
+    assert _step(lib, _ctx(), step=-1) == dgd.DGD_EINVAL
+    assert _step(lib, _ctx(), block=1) == dgd.DGD_EINVAL
+    assert _step(lib, _ctx(), H=None) == dgd.DGD_EINVAL
+    assert _step(lib, _ctx(), W=None) == dgd.DGD_EINVAL
+    p = dgd.make_params(N=8)
+    assert lib.dgd_step(FAKE, FAKE, FAKE, FAKE, 0, 0, ctypes.byref(p), None, ctypes.byref(_ctx())) == dgd.DGD_EINVAL
+    assert lib.dgd_step(FAKE, FAKE, FAKE, FAKE, 0, 0, None, None, ctypes.byref(_ctx())) == dgd.DGD_EINVAL
+    assert lib.dgd_run(FAKE, FAKE, FAKE, FAKE, ctypes.byref(p), None, None) == dgd.DGD_EINVAL
+    s = (ctypes.c_uint64 * 1)(0)
+    assert lib.dgd_init_block(FAKE, FAKE, 3, ctypes.byref(p), s, ctypes.byref(_ctx())) == dgd.DGD_EINVAL
+    assert lib.dgd_init_block(None, FAKE, 0, ctypes.byref(p), s, ctypes.byref(_ctx())) == dgd.DGD_EINVAL
+    assert lib.dgd_debug_gumbel(None, FAKE, 4, None) == dgd.DGD_EINVAL
+    assert lib.dgd_debug_gumbel(FAKE, FAKE, -1, None) == dgd.DGD_EINVAL
+    assert lib.dgd_debug_gumbel(FAKE, FAKE, 0, None) == dgd.DGD_OK
+
+
+def test_binding_refuses_missing_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        dgd._lib, saved = None, dgd._lib
+        try:
+            dgd.load_library(str(tmp_path / "missing.so"))
+        finally:
+            dgd._lib = saved

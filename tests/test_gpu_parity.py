@@ -1,0 +1,162 @@
+"""GPU parity of the HIP step (through the C ABI) with the CPU oracle.
+
+Lockstep comparisons at sizes the oracle finishes in seconds, spanning
+several vocabulary tiles, several 64-element hidden chunks and ragged tails,
+plus the degenerate cases of the method.  Criteria: see tests/parity.py.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import dgd_oracle as O
+from tests.parity import TOL_LOGIT_REL, Lockstep
+from uniform_state_discrete_step_amd.inputs import (WORKLOADS, f32_to_bf16_bits,
+                                                    make_workload_arrays, shrink)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    torch = pytest.importorskip("torch")
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def bf16(x):
+    return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
+
+
+def run_lockstep(wl, dev, W=None, Hs=None, logits=False, **kw):
+    if W is None:
+        W, Hs = make_workload_arrays(wl, threads=8)
+    ls = Lockstep(wl, W, Hs, dev, logits=logits)
+    rep = ls.run(**kw)
+    print(f"\n[{wl.name} B={wl.B} L={wl.L} G={wl.G} V={wl.V} d={wl.d} N={wl.N} "
+          f"freeze={wl.freeze} final_emit={wl.final_emit}] {rep.summary()}", flush=True)
+    assert not rep.failures, "\n".join(rep.failures)
+    return ls, rep
+
+
+# ----------------------------------------------------------------------------
+def test_gumbel_transform_every_cell(dev):
+    """The fused step's noise on all 2^23 uniform cells, against float64."""
+    import torch
+    from uniform_state_discrete_step_amd import dgd
+    k = np.arange(1 << 23, dtype=np.uint32)
+    words = (k << np.uint32(9)) | np.uint32(0x155)
+    wd = torch.from_numpy(words.view(np.int32)).to(dev)
+    out = torch.empty(words.shape[0], dtype=torch.float32, device=dev)
+    dgd.dgd_debug_gumbel(wd, out)
+    g_gpu = out.cpu().numpy().astype(np.float64) * math.log(2) - math.log(math.log(2))
+    g_ref = O.gumbel_from_word(words)
+    err = np.abs(g_gpu - g_ref)
+    worst = int(np.argmax(err))
+    print(f"\nmax |g_gpu - g| = {err[worst]:.3e} at cell {worst} (g = {g_ref[worst]:.6f}); "
+          f"mean {err.mean():.3e}", flush=True)
+    assert err.max() <= 2e-5
+
+
+def test_tiny_lockstep(dev):
+    run_lockstep(WORKLOADS["tiny"], dev)
+
+
+@pytest.mark.parametrize("variant", [
+    dict(B=3, G=32, seeds=(0, 1, 2**63 + 5), bounds=(0.1, 0.0, 1.0)),
+    dict(freeze=0),
+    dict(final_emit=1),
+    dict(stability_threshold=0, confidence=1.0),
+    dict(N=1),
+    dict(N=3, t_min=0.0, t_max=1.0),
+])
+def test_tiny_variants(dev, variant):
+    run_lockstep(shrink(WORKLOADS["tiny"], **variant), dev)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(V=1001, d=72, L=37, B=3, G=74, N=5),     # ragged vocabulary, hidden and rows; 2 blocks
+    dict(V=129, d=8, L=1, B=2, G=3, N=4),          # one-position canvases, 3 blocks
+    dict(V=1, d=16, L=5, B=1, G=5, N=3),           # one-token vocabulary
+    dict(V=4096, d=136, L=70, B=2, G=70, N=6),     # rows straddle 32-row blocks of one tile
+])
+def test_ragged_shapes(dev, shape):
+    B = shape["B"]
+    wl = shrink(WORKLOADS["tiny"], name="ragged", cfg_seed=7, seeds=tuple(range(B)),
+                bounds=tuple((0.1, 0.3, 0.05)[c % 3] for c in range(B)), **shape)
+    run_lockstep(wl, dev)
+
+
+def test_small_vocab_lockstep(dev):
+    run_lockstep(WORKLOADS["small_vocab"], dev)
+
+
+# ----------------------------------------------------------------------------
+def _logit_check(wl, dev, W, Hs, steps):
+    import torch
+    ls = Lockstep(wl, W, Hs, dev, logits=True)
+    ls.run(steps=steps)
+    torch.cuda.synchronize()
+    z_gpu = ls.ctx.logits.cpu().numpy().reshape(wl.B * wl.L, wl.V).astype(np.float64)
+    b, s = wl.blocks - 1, steps[-1]
+    z = O.projection(Hs[b, s].reshape(wl.B * wl.L, wl.d), W)
+    scale = np.maximum(np.abs(z), np.sqrt(np.mean(z * z, axis=1, keepdims=True)))
+    rel = np.abs(z_gpu - z) / np.maximum(scale, 1e-30)
+    print(f"\n[{wl.name}] logits: max rel err {rel.max():.3e}, max abs err "
+          f"{np.abs(z_gpu - z).max():.3e}", flush=True)
+    assert rel.max() <= TOL_LOGIT_REL
+    return z_gpu, z
+
+
+def test_logits_tiny(dev):
+    wl = WORKLOADS["tiny"]
+    W, Hs = make_workload_arrays(wl, threads=1)
+    _logit_check(wl, dev, W, Hs, steps=[0, 1, 2])
+
+
+def test_logits_small_vocab(dev):
+    wl = WORKLOADS["small_vocab"]
+    W, Hs = make_workload_arrays(wl, threads=8)
+    _logit_check(wl, dev, W, Hs, steps=[0])
+
+
+def test_projection_is_exact_on_small_integers(dev):
+    """Small-integer bf16 H and W: every fp32 partial sum is exact, so the
+    logits must equal the exact integer dot products bit for bit (a wrong
+    operand layout, transposition or hidden-chunk mapping cannot pass)."""
+    wl = shrink(WORKLOADS["tiny"], V=300, d=200, L=40, B=1, G=40, N=2)
+    rng = np.random.default_rng(11)
+    W = bf16(rng.integers(-2, 3, size=(wl.V, wl.d)))
+    Hs = bf16(rng.integers(-2, 3, size=(1, wl.N, 1, wl.L, wl.d)))
+    z_gpu, z = _logit_check(wl, dev, W, Hs, steps=[0])
+    assert np.array_equal(z_gpu, z)
+
+
+# ----------------------------------------------------------------------------
+def test_first_step_from_uniform_logits(dev):
+    """H = 0 gives uniform logits: entropy ln V everywhere and one commit, at position 0."""
+    wl = shrink(WORKLOADS["tiny"], V=2048, d=64, L=64, G=64, N=4)
+    W, _ = make_workload_arrays(wl, threads=1)
+    Hs = np.zeros((1, wl.N, 1, wl.L, wl.d), dtype=np.uint16)
+    ls, rep = run_lockstep(wl, dev, W=W, Hs=Hs, steps=[0])
+    H = ls.ctx.entropy.cpu().numpy()
+    assert np.all(np.abs(H - math.log(wl.V)) < 1e-5)
+    com = ls.committed.cpu().numpy()
+    assert com.tolist() == [1] + [0] * (wl.L - 1)
+
+
+def test_convergence_on_stable_peaked_inputs(dev):
+    """Identical one-hot logits every step: the canvas converges at step 1."""
+    V = d = 64
+    L = 32
+    wl = shrink(WORKLOADS["tiny"], V=V, d=d, L=L, G=L, N=8)
+    W = bf16(np.eye(V))
+    toks = (np.arange(L) * 7 + 3) % V
+    h = np.zeros((L, d), dtype=np.float32)
+    h[np.arange(L), toks] = 60.0
+    Hs = np.broadcast_to(bf16(h), (1, wl.N, 1, L, d)).copy()
+    ls, rep = run_lockstep(wl, dev, W=W, Hs=Hs)
+    sv = ls.ctx.state_views()
+    assert int(sv["steps_used"][0]) == 2 and int(sv["converged"][0]) == 1
+    assert np.array_equal(ls.canvas.cpu().numpy(), toks)

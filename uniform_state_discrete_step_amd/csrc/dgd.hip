@@ -1,0 +1,930 @@
+// libdgd: the per-step denoising update of uniform-state discrete diffusion
+// on AMD Instinct MI355X (gfx950, CDNA4).
+//
+// Per step, two kernels:
+//   k_project       bf16 MFMA projection z = H W^T (W streamed once from HBM,
+//                   H chunks staged through LDS) fused with the tempered
+//                   softmax-entropy, argmax and Gumbel-max reductions in its
+//                   epilogue; writes one 32-byte partial record per
+//                   (position, vocabulary group).  Logits stay in registers.
+//   k_merge_commit  merges the partial records of each position, then the
+//                   last workgroup of each canvas applies the early-stop
+//                   rule, sorts the open positions by entropy, applies the
+//                   entropy bound, writes samples and re-noises the rest.
+// plus k_init_block at the start of each block.
+//
+// The method follows "The Annotated DiffusionGemma" walkthrough, section
+// "Sampling" (temperature, entropy, low-entropy prefix, early stop), with the
+// knob semantics of the ComfyUI "DiffusionGemma Denoise (KV Cache)" node page
+// (Inputs table) and the TensorSharp DiffusionGemma doc ("3. Sampler
+// contract").  The C ABI is declared and documented in include/dgd.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/dgd.h"
+#include "dgd_device.h"
+
+using namespace dgd;
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// tiling constants of the projection
+// ---------------------------------------------------------------------------
+constexpr int kThreads = 256;           // 4 waves of 64
+constexpr int kWaves = kThreads / 64;
+constexpr int kVocabPerWave = 32;       // MFMA A rows (vocabulary) per wave
+constexpr int kVocabTile = kWaves * kVocabPerWave;   // 128 vocabulary rows per tile
+constexpr int kKChunk = 64;             // hidden elements per LDS stage
+constexpr int kMaxGroups = 512;         // vocabulary groups (partials per position)
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr double kLn2 = 0.693147180559945309417232121458176568;
+constexpr double kLog2e = 1.442695040888963407359924681001892137;
+
+struct ProjArgs {
+  const uint16_t* H;      // [M][d]
+  const uint16_t* W;      // [V][d]
+  Rec* part;              // [M][P]
+  float* logits;          // [M][V] (validation) or null
+  const int32_t* done;    // [B]
+  int32_t* counters;      // [B], zeroed here for the commit kernel
+  int32_t M, V, d, L, B;
+  int32_t P, n_vtiles, n_mtiles;
+  int32_t block, gstep;
+  float c2;               // log2(e) / T_s
+  uint32_t key[DGD_MAX_CANVASES][2];
+};
+
+struct CommitArgs {
+  const Rec* part;
+  int32_t P;
+  float* rowH;
+  int32_t* rowA;
+  int32_t* rowTok;
+  float* out_entropy;
+  int32_t* out_argmax;
+  int32_t* out_token;
+  float* out_gap;
+  int16_t* commit_step;
+  int32_t* canvas;
+  uint8_t* committed;
+  int32_t* st_prev;
+  int32_t* st_stable;
+  int32_t* st_done;
+  int32_t* st_steps;
+  int32_t* st_conv;
+  int32_t* st_ncomm;
+  float* st_mean;
+  int32_t* st_new;
+  int32_t* counters;
+  int32_t B, L, G, V, N, block, step, gstep, freeze, final_emit, stab;
+  float conf;
+  float bound[DGD_MAX_CANVASES];
+  uint32_t key[DGD_MAX_CANVASES][2];
+};
+
+struct InitArgs {
+  int32_t* canvas;
+  uint8_t* committed;
+  int32_t* st_prev;
+  int32_t* st_stable;
+  int32_t* st_done;
+  int32_t* st_steps;
+  int32_t* st_conv;
+  int32_t* st_ncomm;
+  float* st_mean;
+  int32_t* st_new;
+  int32_t B, L, G, V, block;
+  uint32_t key[DGD_MAX_CANVASES][2];
+};
+
+// Vocabulary groups: tiles vt = g, g + P, g + 2P, ... belong to group g.  The
+// count depends on V only, so a position's merge order never depends on how
+// many canvases are batched together.
+__host__ __device__ inline int num_vtiles(int V) { return (V + kVocabTile - 1) / kVocabTile; }
+__host__ __device__ inline int num_groups(int V) {
+  const int t = num_vtiles(V);
+  return t < kMaxGroups ? t : kMaxGroups;
+}
+
+// Block id -> (M tile, vocabulary group).  Consecutive ids go to different
+// XCDs (round-robin); the ids one XCD receives walk the M tiles of one group
+// before the next group, so tiles that share W rows run on one L2.
+__device__ inline void tile_of_block(int id, int n_mtiles, int P, int& mt, int& g) {
+  if ((P & 7) == 0) {
+    const int xcd = id & 7, j = id >> 3;
+    mt = j % n_mtiles;
+    g = (j / n_mtiles) * 8 + xcd;
+  } else {
+    mt = id % n_mtiles;
+    g = id / n_mtiles;
+  }
+}
+
+__device__ inline bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// ---------------------------------------------------------------------------
+// k_project: fused projection + tempered softmax-entropy / argmax / Gumbel-max
+// ---------------------------------------------------------------------------
+// Workgroup = 4 waves; tile = 128 vocabulary rows (32 per wave) x MROWS = 32*MB
+// positions.  MFMA v_mfma_f32_32x32x16_bf16 with A = W (vocabulary along the
+// MFMA rows) and B = H (positions along the MFMA columns), so lane l of a
+// wave holds, per 32-position block, 16 logits of ONE position (column l%32)
+// at vocabulary rows 8q + 4(l/32) + e (q, e = 0..3): four groups of four
+// consecutive vocabulary ids, i.e. exactly the four words of one Philox call.
+//
+// K loop: per 64-element hidden chunk each lane loads the 64 contiguous
+// bytes W[v][32h .. 32h+31] (h = lane/32) and the workgroup stages the
+// [MROWS x 64] H chunk in LDS (double buffered, 16-byte segments XOR-swizzled
+// by row).  MFMA sub-step s (0..3) uses hidden elements 32h + 8s .. +7 for
+// lane half h in both operands: the same permutation of k on A and B, so the
+// products summed are exactly those of the plain dot product.
+template <int MB, bool kLogits>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MB >= 8 ? 1 : 2)))
+k_project(const ProjArgs a) {
+  constexpr int MROWS = 32 * MB;
+  constexpr int HSEG = MROWS * (kKChunk / 8) / kThreads;   // 16-byte H segments per thread
+  constexpr int NREC = MB >= 2 ? MB / 2 : 1;
+  static_assert(HSEG >= 1, "tile too small");
+  static_assert(kWaves * MROWS * (int)sizeof(Rec) <= 2 * MROWS * kKChunk * 2, "LDS reuse");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * MROWS * kKChunk * 2];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+
+  if (blockIdx.x == 0 && tid < a.B) a.counters[tid] = 0;
+
+  int mt, g;
+  tile_of_block(blockIdx.x, a.n_mtiles, a.P, mt, g);
+  const int row0 = mt * MROWS;
+  {
+    const int last_row = min(row0 + MROWS, a.M) - 1;
+    bool all_done = true;
+    for (int c = row0 / a.L; c <= last_row / a.L; ++c) all_done &= (a.done[c] != 0);
+    if (all_done) return;
+  }
+
+  Rec run[NREC];
+#pragma unroll
+  for (int i = 0; i < NREC; ++i) run[i] = rec_empty();
+
+  const int nk = (a.d + kKChunk - 1) / kKChunk;
+  const size_t d = (size_t)a.d;
+
+  for (int vt = g; vt < a.n_vtiles; vt += a.P) {
+    const int vbase = vt * kVocabTile + wave * kVocabPerWave;
+    const int vlane = vbase + col;
+    const bool wvalid = vlane < a.V;
+    const uint16_t* wrow = a.W + (size_t)(wvalid ? vlane : 0) * d;
+
+    auto load_w = [&](int c, u32x4_t (&dst)[4]) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int kel = c * kKChunk + 32 * half + 8 * s;
+        if (wvalid && kel < a.d)
+          dst[s] = __builtin_nontemporal_load((const u32x4_t*)(wrow + kel));
+        else
+          dst[s] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    };
+    auto load_h = [&](int c, u32x4_t (&dst)[HSEG]) {
+#pragma unroll
+      for (int i = 0; i < HSEG; ++i) {
+        const int idx = i * kThreads + tid;
+        const int r = idx >> 3, e = idx & 7;
+        const int grow = row0 + r;
+        const int kel = c * kKChunk + e * 8;
+        if (grow < a.M && kel < a.d)
+          dst[i] = *(const u32x4_t*)(a.H + (size_t)grow * d + kel);
+        else
+          dst[i] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    };
+    auto store_h = [&](int buf, const u32x4_t (&src)[HSEG]) {
+      uint8_t* base = smem + buf * (MROWS * kKChunk * 2);
+#pragma unroll
+      for (int i = 0; i < HSEG; ++i) {
+        const int idx = i * kThreads + tid;
+        const int r = idx >> 3, e = idx & 7;
+        *(u32x4_t*)(base + r * 128 + ((e ^ (r & 7)) << 4)) = src[i];
+      }
+    };
+
+    f32x16_t acc[MB];
+#pragma unroll
+    for (int pb = 0; pb < MB; ++pb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[pb][i] = 0.f;
+
+    u32x4_t wc[4], wn[4], hs[HSEG];
+    __syncthreads();   // previous tile's readers of smem are done
+    load_w(0, wc);
+    load_h(0, hs);
+    store_h(0, hs);
+    __syncthreads();
+
+    for (int c = 0; c < nk; ++c) {
+      const int buf = c & 1;
+      const bool more = c + 1 < nk;
+      if (more) {
+        load_h(c + 1, hs);
+        load_w(c + 1, wn);
+      }
+      const uint8_t* hb = smem + buf * (MROWS * kKChunk * 2);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const bf16x8_t av = as_bf16x8(wc[s]);
+#pragma unroll
+        for (int pb = 0; pb < MB; ++pb) {
+          const int r = pb * 32 + col;
+          const int e = (4 * half + s) ^ (col & 7);
+          const u32x4_t bv = *(const u32x4_t*)(hb + r * 128 + (e << 4));
+          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_bf16x8(bv), acc[pb], 0, 0, 0);
+        }
+      }
+      if (more) {
+        store_h(buf ^ 1, hs);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) wc[s] = wn[s];
+      }
+      __syncthreads();
+    }
+
+    // ---------------- epilogue: one position per lane per block ----------
+#pragma unroll
+    for (int pb = 0; pb < MB; ++pb) {
+      const int r = row0 + pb * 32 + col;
+      const bool rvalid = r < a.M;
+      const int cv = rvalid ? r / a.L : 0;
+      const int p = r - cv * a.L;
+      const uint32_t pabs = (uint32_t)(a.block * a.L + p);
+      const uint32_t key0 = a.key[cv][0], key1 = a.key[cv][1];
+
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = acc[pb][i] * a.c2;
+
+      if constexpr (kLogits) {
+        if (rvalid) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int v0 = vbase + 8 * q + 4 * half;
+            float* dst = a.logits + (size_t)r * a.V + v0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (v0 + e < a.V) dst[e] = acc[pb][4 * q + e];
+          }
+        }
+      }
+
+      float m = kNeg;
+      int am = kNoIndex;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int v = vbase + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (v < a.V && x[i] > m) { m = x[i]; am = v; }
+      }
+      float S = 0.f, A = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int v = vbase + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (v < a.V) {
+          const float dx = x[i] - m;
+          const float e = fexp2(dx);
+          S += e;
+          A += dx * e;
+        }
+      }
+      float y1 = kNeg, y2 = kNeg;
+      int i1 = kNoIndex;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int v0 = vbase + 8 * q + 4 * half;
+        const Philox4 pw = philox4x32_10((uint32_t)v0 >> 2, pabs, (uint32_t)a.gstep, 0u, key0, key1);
+        const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (v0 + e < a.V) {
+            const float y = x[4 * q + e] + gumbel_bits(words[e]);
+            if (y > y1) { y2 = y1; y1 = y; i1 = v0 + e; }
+            else if (y > y2) { y2 = y; }
+          }
+        }
+      }
+      Rec loc;
+      loc.m = m; loc.S = S; loc.A = A; loc.am = am;
+      loc.y1 = y1; loc.i1 = i1; loc.y2 = y2; loc.pad = 0.f;
+      const Rec oth = rec_shfl_xor(loc, 32);
+      const Rec wrec = rec_merge(rec_pick(half == 0, loc, oth), rec_pick(half == 0, oth, loc));
+      if constexpr (MB == 1) {
+        if (half == 0) run[0] = rec_merge(run[0], wrec);
+      } else {
+        if (half == (pb & 1)) run[pb >> 1] = rec_merge(run[pb >> 1], wrec);
+      }
+    }
+  }
+
+  // ---------------- merge the four waves (fixed order) and write ----------
+  __syncthreads();
+  Rec* rl = reinterpret_cast<Rec*>(smem);
+#pragma unroll
+  for (int pb = 0; pb < MB; ++pb) {
+    const bool own = (MB == 1) ? (half == 0) : (half == (pb & 1));
+    if (own) rec_store(rl + wave * MROWS + pb * 32 + col, run[MB == 1 ? 0 : (pb >> 1)]);
+  }
+  __syncthreads();
+  for (int t = tid; t < MROWS; t += kThreads) {
+    Rec r = rec_load(rl + t);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = rec_merge(r, rec_load(rl + w * MROWS + t));
+    const int row = row0 + t;
+    if (row < a.M) rec_store(a.part + (size_t)row * a.P + g, r);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_merge_commit
+// ---------------------------------------------------------------------------
+__device__ inline double block_sum_f64(double v, double* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const double out = red[0];
+  __syncthreads();
+  return out;
+}
+
+__device__ inline int block_sum_i32(int v, int* red) {
+  const int tid = threadIdx.x;
+  red[tid] = v;
+  __syncthreads();
+  for (int s = kThreads / 2; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const int out = red[0];
+  __syncthreads();
+  return out;
+}
+
+// Commit phase of one canvas, run by the whole (last) workgroup.
+__device__ void commit_canvas(const CommitArgs& a, int c) {
+  __shared__ unsigned long long keys[DGD_MAX_CANVAS_LEN];
+  __shared__ double dred[kThreads];
+  __shared__ int ired[kThreads];
+  const int tid = threadIdx.x;
+  const int L = a.L;
+  const size_t rbase = (size_t)c * L;
+  const size_t cbase = (size_t)c * a.G + (size_t)a.block * L;
+
+  // early stop: mean entropy over the block and argmax stability
+  double hsum = 0.0;
+  int moved = 0;
+  for (int p = tid; p < L; p += kThreads) {
+    hsum += (double)a.rowH[rbase + p];
+    moved += (a.rowA[rbase + p] != a.st_prev[rbase + p]);
+  }
+  const double mean = block_sum_f64(hsum, dred) / (double)L;
+  const bool stable = block_sum_i32(moved, ired) == 0;
+  const int sc = stable ? a.st_stable[c] + 1 : 0;
+  const bool converged = mean < (double)a.conf && sc >= a.stab;
+  const bool final_step = converged || a.step == a.N - 1;
+
+  int new_commits = 0, open_before = 0;
+  if (final_step) {
+    for (int p = tid; p < L; p += kThreads) {
+      const size_t idx = cbase + p;
+      const bool open = a.committed[idx] == 0;
+      open_before += open;
+      if (a.freeze == 0 || open) {
+        a.canvas[idx] = a.final_emit ? a.rowA[rbase + p] : a.rowTok[rbase + p];
+        a.committed[idx] = 1;
+        if (a.commit_step) a.commit_step[idx] = (int16_t)a.step;
+        new_commits += open;
+      }
+    }
+    new_commits = block_sum_i32(new_commits, ired);
+    if (tid == 0) {
+      a.st_done[c] = 1;
+      a.st_conv[c] = converged ? 1 : 0;
+      a.st_ncomm[c] = L;
+    }
+  } else {
+    int n2 = 1;
+    while (n2 < L) n2 <<= 1;
+    int elig = 0;
+    for (int i = tid; i < n2; i += kThreads) {
+      unsigned long long k = ~0ull;
+      if (i < L && (a.freeze == 0 || a.committed[cbase + i] == 0)) {
+        k = ((unsigned long long)__float_as_uint(a.rowH[rbase + i]) << 32) | (unsigned)i;
+        ++elig;
+      }
+      keys[i] = k;
+    }
+    const int n_elig = block_sum_i32(elig, ired);   // also orders the key writes
+    // bitonic sort, ascending (entropy bits are monotone: entropies are >= 0)
+    for (int k = 2; k <= n2; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < n2; i += kThreads) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const unsigned long long ki = keys[i], kj = keys[ixj];
+            const bool up = (i & k) == 0;
+            if ((ki > kj) == up) { keys[i] = kj; keys[ixj] = ki; }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    // exclusive float64 running sum over ranks: contiguous chunk per thread
+    const int per = (n2 + kThreads - 1) / kThreads;
+    const int r0 = tid * per;
+    double loc = 0.0;
+    for (int k = 0; k < per; ++k) {
+      const int rk = r0 + k;
+      if (rk < n_elig) loc += (double)__uint_as_float((unsigned)(keys[rk] >> 32));
+    }
+    dred[tid] = loc;
+    __syncthreads();
+    if (tid == 0) {
+      double run = 0.0;
+      for (int t = 0; t < kThreads; ++t) {
+        const double v = dred[t];
+        dred[t] = run;
+        run += v;
+      }
+    }
+    __syncthreads();
+    double E = dred[tid];
+    const double bound = (double)a.bound[c];
+    const uint32_t k0 = a.key[c][0], k1 = a.key[c][1];
+    for (int k = 0; k < per; ++k) {
+      const int rk = r0 + k;
+      if (rk >= n_elig) break;
+      const unsigned long long key = keys[rk];
+      const int p = (int)(key & 0xffffffffu);
+      const float h = __uint_as_float((unsigned)(key >> 32));
+      const size_t idx = cbase + p;
+      if (E <= bound) {
+        a.canvas[idx] = a.rowTok[rbase + p];
+        a.committed[idx] = 1;
+        if (a.commit_step) a.commit_step[idx] = (int16_t)a.step;
+        ++new_commits;
+      } else {
+        const uint32_t pabs = (uint32_t)(a.block * L + p);
+        const Philox4 w = philox4x32_10(0u, pabs, (uint32_t)a.gstep, 1u, k0, k1);
+        a.canvas[idx] = word_to_token(w.x, (uint32_t)a.V);
+        a.committed[idx] = 0;
+      }
+      E += (double)h;
+    }
+    new_commits = block_sum_i32(new_commits, ired);
+    if (tid == 0) {
+      a.st_conv[c] = 0;
+      a.st_ncomm[c] = (a.freeze ? (L - n_elig) : 0) + new_commits;
+    }
+  }
+  (void)open_before;
+  if (tid == 0) {
+    a.st_stable[c] = sc;
+    a.st_steps[c] = a.step + 1;
+    a.st_mean[c] = (float)mean;
+    a.st_new[c] = new_commits;
+  }
+  // the argmax canvas of this step becomes the reference of the next one
+  for (int p = tid; p < L; p += kThreads) a.st_prev[rbase + p] = a.rowA[rbase + p];
+}
+
+// Grid (ceil(L/4), B); one wave per position merges that position's partial
+// records; the last workgroup of each canvas commits it.
+__global__ void __launch_bounds__(kThreads) k_merge_commit(const CommitArgs a) {
+  const int c = blockIdx.y;
+  if (a.st_done[c]) return;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int p = blockIdx.x * kWaves + wave;
+  if (p < a.L) {
+    const size_t r = (size_t)c * a.L + p;
+    const Rec* pr = a.part + r * a.P;
+    Rec rec = rec_empty();
+    for (int i = lane; i < a.P; i += 64) rec = rec_merge(rec, rec_load(pr + i));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      const Rec o = rec_shfl_xor(rec, off);
+      const bool upper = (lane & off) != 0;
+      rec = rec_merge(rec_pick(upper, o, rec), rec_pick(upper, rec, o));
+    }
+    if (lane == 0) {
+      const double S = (double)rec.S, A = (double)rec.A;
+      double Hn = kLn2 * (log2(S) - A / S);
+      if (!(Hn > 0.0)) Hn = 0.0;
+      const float H = (float)Hn;
+      const float gap = (float)(((double)rec.y1 - (double)rec.y2) * kLn2);
+      a.rowH[r] = H;
+      a.rowA[r] = rec.am;
+      a.rowTok[r] = rec.i1;
+      if (a.out_entropy) a.out_entropy[r] = H;
+      if (a.out_argmax) a.out_argmax[r] = rec.am;
+      if (a.out_token) a.out_token[r] = rec.i1;
+      if (a.out_gap) a.out_gap[r] = gap;
+    }
+  }
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = (atomicAdd(&a.counters[c], 1) == (int)gridDim.x - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  commit_canvas(a, c);
+}
+
+// Grid (ceil(L/256), B).
+__global__ void __launch_bounds__(kThreads) k_init_block(const InitArgs a) {
+  const int c = blockIdx.y;
+  const int p = blockIdx.x * kThreads + threadIdx.x;
+  if (p < a.L) {
+    const uint32_t pabs = (uint32_t)(a.block * a.L + p);
+    const size_t idx = (size_t)c * a.G + pabs;
+    const Philox4 w = philox4x32_10(0u, pabs, (uint32_t)a.block, 2u, a.key[c][0], a.key[c][1]);
+    a.canvas[idx] = word_to_token(w.x, (uint32_t)a.V);
+    a.committed[idx] = 0;
+    a.st_prev[(size_t)c * a.L + p] = 0;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    a.st_stable[c] = 0;
+    a.st_done[c] = 0;
+    a.st_steps[c] = 0;
+    a.st_conv[c] = 0;
+    a.st_ncomm[c] = 0;
+    a.st_mean[c] = 0.f;
+    a.st_new[c] = 0;
+  }
+}
+
+__global__ void k_debug_gumbel(const uint32_t* words, float* out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = gumbel_bits(words[i]);
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(DGD_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct WsLayout {
+  size_t part, rowH, rowA, rowTok, counters, total;
+  int P;
+};
+
+WsLayout ws_layout(int B, int L, int V) {
+  WsLayout w{};
+  const size_t M = (size_t)B * L;
+  w.P = num_groups(V);
+  size_t off = 0;
+  w.part = off;     off = align256(off + M * (size_t)w.P * sizeof(Rec));
+  w.rowH = off;     off = align256(off + M * sizeof(float));
+  w.rowA = off;     off = align256(off + M * sizeof(int32_t));
+  w.rowTok = off;   off = align256(off + M * sizeof(int32_t));
+  w.counters = off; off = align256(off + (size_t)B * sizeof(int32_t));
+  w.total = off;
+  return w;
+}
+
+struct StateView {
+  int32_t *prev, *stable, *done, *steps, *conv, *ncomm, *newc;
+  float* mean;
+};
+
+StateView state_view(void* state, int B, int L) {
+  int32_t* s = (int32_t*)state;
+  const size_t BL = (size_t)B * L;
+  StateView v;
+  v.prev = s;
+  v.stable = s + BL;
+  v.done = s + BL + B;
+  v.steps = s + BL + 2 * (size_t)B;
+  v.conv = s + BL + 3 * (size_t)B;
+  v.ncomm = s + BL + 4 * (size_t)B;
+  v.mean = (float*)(s + BL + 5 * (size_t)B);
+  v.newc = s + BL + 6 * (size_t)B;
+  return v;
+}
+
+bool finite01(float x) { return std::isfinite(x) && x >= 0.f && x <= 1.f; }
+
+int check_shape(const dgd_ctx* ctx) {
+  if (!ctx) return fail(DGD_EINVAL, "ctx is NULL");
+  if (ctx->B < 1 || ctx->B > DGD_MAX_CANVASES)
+    return fail(DGD_EUNSUPPORTED, "B=%d outside [1, %d]", ctx->B, DGD_MAX_CANVASES);
+  if (ctx->L < 1 || ctx->L > DGD_MAX_CANVAS_LEN)
+    return fail(DGD_EUNSUPPORTED, "L=%d outside [1, %d]", ctx->L, DGD_MAX_CANVAS_LEN);
+  if (ctx->G < ctx->L || ctx->G > DGD_MAX_GEN_LENGTH || ctx->G % ctx->L != 0)
+    return fail(DGD_EINVAL, "G=%d must be a multiple of L=%d in [L, %d]", ctx->G, ctx->L,
+                DGD_MAX_GEN_LENGTH);
+  if (ctx->V < 1 || ctx->V > DGD_MAX_VOCAB)
+    return fail(DGD_EUNSUPPORTED, "V=%d outside [1, 2^24]", ctx->V);
+  if (ctx->d < 8 || ctx->d > DGD_MAX_HIDDEN || ctx->d % 8 != 0)
+    return fail(DGD_EUNSUPPORTED, "d=%d must be a multiple of 8 in [8, %d]", ctx->d,
+                DGD_MAX_HIDDEN);
+  if (!ctx->state) return fail(DGD_EINVAL, "ctx->state is NULL");
+  return DGD_OK;
+}
+
+int check_params(const dgd_params* prm) {
+  if (!prm) return fail(DGD_EINVAL, "params is NULL");
+  const int N = prm->num_inference_steps;
+  if (N < 1 || N > DGD_MAX_STEPS) return fail(DGD_EINVAL, "num_inference_steps=%d outside [1, 1024]", N);
+  if (!finite01(prm->t_min) || !finite01(prm->t_max))
+    return fail(DGD_EINVAL, "t_min=%g / t_max=%g must be finite and in [0, 1]", prm->t_min, prm->t_max);
+  const double tlast = (double)prm->t_max + ((double)(N - 1) / N) * ((double)prm->t_min - prm->t_max);
+  if (!(prm->t_max > 0.f) || !(tlast > 0.0))
+    return fail(DGD_EINVAL, "temperature schedule reaches T <= 0 (t_min=%g, t_max=%g)", prm->t_min,
+                prm->t_max);
+  if (!finite01(prm->confidence)) return fail(DGD_EINVAL, "confidence=%g outside [0, 1]", prm->confidence);
+  if (prm->stability_threshold < 0 || prm->stability_threshold > DGD_MAX_STEPS)
+    return fail(DGD_EINVAL, "stability_threshold=%d outside [0, 1024]", prm->stability_threshold);
+  if (prm->freeze != 0 && prm->freeze != 1) return fail(DGD_EINVAL, "freeze must be 0 or 1");
+  if (prm->final_emit != 0 && prm->final_emit != 1) return fail(DGD_EINVAL, "final_emit must be 0 or 1");
+  return DGD_OK;
+}
+
+int check_knobs(const dgd_ctx* ctx, const uint64_t* seed, bool need_bounds) {
+  if (!seed) return fail(DGD_EINVAL, "seed is NULL");
+  if (need_bounds) {
+    if (!ctx->entropy_bound) return fail(DGD_EINVAL, "ctx->entropy_bound is NULL");
+    for (int c = 0; c < ctx->B; ++c)
+      if (!finite01(ctx->entropy_bound[c]))
+        return fail(DGD_EINVAL, "entropy_bound[%d]=%g outside [0, 1]", c, ctx->entropy_bound[c]);
+  }
+  return DGD_OK;
+}
+
+int check_workspace(const dgd_ctx* ctx) {
+  const WsLayout w = ws_layout(ctx->B, ctx->L, ctx->V);
+  if (!ctx->workspace) return fail(DGD_EINVAL, "ctx->workspace is NULL");
+  if (((uintptr_t)ctx->workspace & 255) != 0) return fail(DGD_EINVAL, "workspace is not 256-byte aligned");
+  if (ctx->workspace_bytes < w.total)
+    return fail(DGD_EWORKSPACE, "workspace has %zu bytes, needs %zu", ctx->workspace_bytes, w.total);
+  return DGD_OK;
+}
+
+void fill_keys(uint32_t (*key)[2], const uint64_t* seed, int B) {
+  for (int c = 0; c < B; ++c) {
+    key[c][0] = (uint32_t)(seed[c] & 0xffffffffu);
+    key[c][1] = (uint32_t)(seed[c] >> 32);
+  }
+}
+
+int launch_init(int32_t* canvas, uint8_t* committed, int block, const uint64_t* seed,
+                const dgd_ctx* ctx) {
+  InitArgs a{};
+  a.canvas = canvas;
+  a.committed = committed;
+  const StateView sv = state_view(ctx->state, ctx->B, ctx->L);
+  a.st_prev = sv.prev; a.st_stable = sv.stable; a.st_done = sv.done; a.st_steps = sv.steps;
+  a.st_conv = sv.conv; a.st_ncomm = sv.ncomm; a.st_mean = sv.mean; a.st_new = sv.newc;
+  a.B = ctx->B; a.L = ctx->L; a.G = ctx->G; a.V = ctx->V; a.block = block;
+  fill_keys(a.key, seed, ctx->B);
+  const dim3 grid((ctx->L + kThreads - 1) / kThreads, ctx->B);
+  hipLaunchKernelGGL(k_init_block, grid, dim3(kThreads), 0, (hipStream_t)ctx->stream, a);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_init_block launch");
+}
+
+struct Timer {
+  std::vector<hipEvent_t> ev;
+  bool on = false;
+  int begin(hipStream_t s) {
+    if (!on) return DGD_OK;
+    hipEvent_t e;
+    hipError_t r = hipEventCreate(&e);
+    if (r != hipSuccess) return hip_fail(r, "hipEventCreate");
+    ev.push_back(e);
+    r = hipEventRecord(e, s);
+    return r == hipSuccess ? DGD_OK : hip_fail(r, "hipEventRecord");
+  }
+  int finish(const dgd_ctx* ctx) {
+    if (!on) return DGD_OK;
+    double total = 0.0;
+    int n = 0;
+    int rc = DGD_OK;
+    if (!ev.empty()) {
+      hipError_t r = hipEventSynchronize(ev.back());
+      if (r != hipSuccess) rc = hip_fail(r, "hipEventSynchronize");
+      for (size_t i = 0; rc == DGD_OK && i + 1 < ev.size(); i += 2) {
+        float ms = 0.f;
+        r = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
+        if (r != hipSuccess) { rc = hip_fail(r, "hipEventElapsedTime"); break; }
+        total += ms;
+        ++n;
+      }
+    }
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    ev.clear();
+    if (rc == DGD_OK) {
+      *ctx->k1_ms = total;
+      if (ctx->k1_launches) *ctx->k1_launches = n;
+    }
+    return rc;
+  }
+};
+
+template <int MB>
+void launch_project_mb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits) {
+  if (logits)
+    hipLaunchKernelGGL((k_project<MB, true>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_project<MB, false>), grid, dim3(kThreads), 0, s, a);
+}
+
+int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* committed,
+                int block, int step, const dgd_params* prm, const uint64_t* seed,
+                const dgd_ctx* ctx, Timer& timer) {
+  const int B = ctx->B, L = ctx->L, V = ctx->V, dd = ctx->d;
+  const int M = B * L;
+  const int N = prm->num_inference_steps;
+  const WsLayout wl = ws_layout(B, L, V);
+  uint8_t* ws = (uint8_t*)ctx->workspace;
+  const StateView sv = state_view(ctx->state, B, L);
+  hipStream_t stream = (hipStream_t)ctx->stream;
+  const int gstep = block * N + step;
+  const double T = (double)prm->t_max + ((double)step / N) * ((double)prm->t_min - prm->t_max);
+
+  ProjArgs pa{};
+  pa.H = H; pa.W = W;
+  pa.part = (Rec*)(ws + wl.part);
+  pa.logits = ctx->logits;
+  pa.done = sv.done;
+  pa.counters = (int32_t*)(ws + wl.counters);
+  pa.M = M; pa.V = V; pa.d = dd; pa.L = L; pa.B = B;
+  pa.P = wl.P;
+  pa.n_vtiles = num_vtiles(V);
+  pa.block = block; pa.gstep = gstep;
+  pa.c2 = (float)(kLog2e / T);
+  fill_keys(pa.key, seed, B);
+  const int MB = M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8;
+  pa.n_mtiles = (M + 32 * MB - 1) / (32 * MB);
+  const dim3 grid1(pa.n_mtiles * pa.P);
+  int rc = timer.begin(stream);
+  if (rc) return rc;
+  const bool lg = ctx->logits != nullptr;
+  switch (MB) {
+    case 1: launch_project_mb<1>(pa, grid1, stream, lg); break;
+    case 2: launch_project_mb<2>(pa, grid1, stream, lg); break;
+    case 4: launch_project_mb<4>(pa, grid1, stream, lg); break;
+    default: launch_project_mb<8>(pa, grid1, stream, lg); break;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "k_project launch");
+  rc = timer.begin(stream);
+  if (rc) return rc;
+
+  CommitArgs ca{};
+  ca.part = pa.part; ca.P = wl.P;
+  ca.rowH = (float*)(ws + wl.rowH);
+  ca.rowA = (int32_t*)(ws + wl.rowA);
+  ca.rowTok = (int32_t*)(ws + wl.rowTok);
+  ca.out_entropy = ctx->entropy; ca.out_argmax = ctx->argmax;
+  ca.out_token = ctx->token; ca.out_gap = ctx->gap;
+  ca.commit_step = ctx->commit_step;
+  ca.canvas = canvas; ca.committed = committed;
+  ca.st_prev = sv.prev; ca.st_stable = sv.stable; ca.st_done = sv.done; ca.st_steps = sv.steps;
+  ca.st_conv = sv.conv; ca.st_ncomm = sv.ncomm; ca.st_mean = sv.mean; ca.st_new = sv.newc;
+  ca.counters = pa.counters;
+  ca.B = B; ca.L = L; ca.G = ctx->G; ca.V = V; ca.N = N;
+  ca.block = block; ca.step = step; ca.gstep = gstep;
+  ca.freeze = prm->freeze; ca.final_emit = prm->final_emit; ca.stab = prm->stability_threshold;
+  ca.conf = prm->confidence;
+  for (int c = 0; c < B; ++c) ca.bound[c] = ctx->entropy_bound[c];
+  fill_keys(ca.key, seed, B);
+  const dim3 grid2((L + kWaves - 1) / kWaves, B);
+  hipLaunchKernelGGL(k_merge_commit, grid2, dim3(kThreads), 0, stream, ca);
+  e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_merge_commit launch");
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+const char* dgd_last_error(void) { return g_err.c_str(); }
+
+size_t dgd_state_bytes(int32_t B, int32_t L) {
+  if (B < 1 || L < 1) return 0;
+  return ((size_t)B * L + 7 * (size_t)B) * 4;
+}
+
+size_t dgd_workspace_bytes(int32_t B, int32_t L, int32_t V, int32_t d) {
+  if (B < 1 || B > DGD_MAX_CANVASES || L < 1 || L > DGD_MAX_CANVAS_LEN || V < 1 ||
+      V > DGD_MAX_VOCAB || d < 8 || d > DGD_MAX_HIDDEN || d % 8 != 0)
+    return 0;
+  return ws_layout(B, L, V).total;
+}
+
+int dgd_init_block(int32_t* canvas, uint8_t* committed, int32_t block, const dgd_params* params,
+                   const uint64_t* seed, const dgd_ctx* ctx) {
+  g_err.clear();
+  int rc = check_shape(ctx);
+  if (rc) return rc;
+  if ((rc = check_params(params))) return rc;
+  if ((rc = check_knobs(ctx, seed, false))) return rc;
+  if (!canvas || !committed) return fail(DGD_EINVAL, "canvas/committed is NULL");
+  if (block < 0 || block >= ctx->G / ctx->L)
+    return fail(DGD_EINVAL, "block=%d outside [0, %d)", block, ctx->G / ctx->L);
+  return launch_init(canvas, committed, block, seed, ctx);
+}
+
+int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_t* committed,
+             int32_t block, int32_t step, const dgd_params* params, const uint64_t* seed,
+             const dgd_ctx* ctx) {
+  g_err.clear();
+  int rc = check_shape(ctx);
+  if (rc) return rc;
+  if ((rc = check_params(params))) return rc;
+  if ((rc = check_knobs(ctx, seed, true))) return rc;
+  if ((rc = check_workspace(ctx))) return rc;
+  if (!H || !W_vocab || !canvas || !committed) return fail(DGD_EINVAL, "H/W_vocab/canvas/committed is NULL");
+  if (block < 0 || block >= ctx->G / ctx->L)
+    return fail(DGD_EINVAL, "block=%d outside [0, %d)", block, ctx->G / ctx->L);
+  if (step < 0 || step >= params->num_inference_steps)
+    return fail(DGD_EINVAL, "step=%d outside [0, %d)", step, params->num_inference_steps);
+  Timer timer;
+  timer.on = ctx->k1_ms != nullptr;
+  rc = launch_step(H, W_vocab, canvas, committed, block, step, params, seed, ctx, timer);
+  const int rt = timer.finish(ctx);
+  return rc ? rc : rt;
+}
+
+int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas, uint8_t* committed,
+            const dgd_params* params, const uint64_t* seed, const dgd_ctx* ctx) {
+  g_err.clear();
+  int rc = check_shape(ctx);
+  if (rc) return rc;
+  if ((rc = check_params(params))) return rc;
+  if ((rc = check_knobs(ctx, seed, true))) return rc;
+  if ((rc = check_workspace(ctx))) return rc;
+  if (!H_steps || !W_vocab || !canvas || !committed)
+    return fail(DGD_EINVAL, "H_steps/W_vocab/canvas/committed is NULL");
+  const int N = params->num_inference_steps;
+  const int blocks = ctx->G / ctx->L;
+  const size_t step_elems = (size_t)ctx->B * ctx->L * ctx->d;
+  Timer timer;
+  timer.on = ctx->k1_ms != nullptr;
+  for (int b = 0; b < blocks && rc == DGD_OK; ++b) {
+    rc = launch_init(canvas, committed, b, seed, ctx);
+    for (int s = 0; s < N && rc == DGD_OK; ++s)
+      rc = launch_step(H_steps + ((size_t)b * N + s) * step_elems, W_vocab, canvas, committed, b, s,
+                       params, seed, ctx, timer);
+  }
+  const int rt = timer.finish(ctx);
+  return rc ? rc : rt;
+}
+
+int dgd_debug_gumbel(const uint32_t* words, float* out, int64_t n, void* stream) {
+  g_err.clear();
+  if (!words || !out) return fail(DGD_EINVAL, "words/out is NULL");
+  if (n < 0) return fail(DGD_EINVAL, "n < 0");
+  if (n == 0) return DGD_OK;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffff) return fail(DGD_EUNSUPPORTED, "n too large");
+  hipLaunchKernelGGL(k_debug_gumbel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     words, out, n);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_debug_gumbel launch");
+}
+
+}  // extern "C"

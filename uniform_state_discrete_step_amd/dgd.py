@@ -1,0 +1,249 @@
+"""ctypes binding of libdgd.so (the HIP denoising-step library).
+
+Argument marshalling only: every step of the method runs in the library's
+HIP kernels.  The functions keep the C names of include/dgd.h and take torch
+tensors (device memory and streams come from PyTorch); there is no fallback of
+any kind, and calling into a missing library raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdgd.so")
+
+DGD_OK = 0
+DGD_EINVAL = -1
+DGD_EUNSUPPORTED = -2
+DGD_EWORKSPACE = -3
+DGD_EHIP = -4
+DGD_MAX_CANVASES = 64
+DGD_MAX_CANVAS_LEN = 4096
+
+EXPORTED = ("dgd_state_bytes", "dgd_workspace_bytes", "dgd_init_block", "dgd_step", "dgd_run",
+            "dgd_debug_gumbel", "dgd_last_error")
+
+
+class DgdError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libdgd error {code}: {msg}")
+        self.code = code
+
+
+class DgdParams(ctypes.Structure):
+    _fields_ = [
+        ("num_inference_steps", ctypes.c_int32),
+        ("t_min", ctypes.c_float),
+        ("t_max", ctypes.c_float),
+        ("confidence", ctypes.c_float),
+        ("stability_threshold", ctypes.c_int32),
+        ("freeze", ctypes.c_int32),
+        ("final_emit", ctypes.c_int32),
+    ]
+
+
+class DgdCtx(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("L", ctypes.c_int32), ("V", ctypes.c_int32),
+        ("d", ctypes.c_int32), ("G", ctypes.c_int32),
+        ("entropy_bound", ctypes.POINTER(ctypes.c_float)),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_size_t),
+        ("state", ctypes.c_void_p),
+        ("stream", ctypes.c_void_p),
+        ("entropy", ctypes.c_void_p),
+        ("argmax", ctypes.c_void_p),
+        ("token", ctypes.c_void_p),
+        ("gap", ctypes.c_void_p),
+        ("logits", ctypes.c_void_p),
+        ("commit_step", ctypes.c_void_p),
+        ("k1_ms", ctypes.POINTER(ctypes.c_double)),
+        ("k1_launches", ctypes.POINTER(ctypes.c_int32)),
+    ]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libdgd.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    lib.dgd_state_bytes.restype = ctypes.c_size_t
+    lib.dgd_state_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.dgd_workspace_bytes.restype = ctypes.c_size_t
+    lib.dgd_workspace_bytes.argtypes = [ctypes.c_int32] * 4
+    lib.dgd_last_error.restype = ctypes.c_char_p
+    lib.dgd_last_error.argtypes = []
+    pp = ctypes.POINTER(DgdParams)
+    pc = ctypes.POINTER(DgdCtx)
+    pseed = ctypes.POINTER(ctypes.c_uint64)
+    lib.dgd_init_block.restype = ctypes.c_int
+    lib.dgd_init_block.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, pp, pseed, pc]
+    lib.dgd_step.restype = ctypes.c_int
+    lib.dgd_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                             ctypes.c_int32, ctypes.c_int32, pp, pseed, pc]
+    lib.dgd_run.restype = ctypes.c_int
+    lib.dgd_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                            pp, pseed, pc]
+    lib.dgd_debug_gumbel.restype = ctypes.c_int
+    lib.dgd_debug_gumbel.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                     ctypes.c_void_p]
+    _lib = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != DGD_OK:
+        raise DgdError(rc, load_library().dgd_last_error().decode())
+
+
+def make_params(N=48, t_min=0.4, t_max=0.8, confidence=0.005, stability_threshold=1, freeze=1,
+                final_emit=0) -> DgdParams:
+    return DgdParams(int(N), float(t_min), float(t_max), float(confidence),
+                     int(stability_threshold), int(freeze), int(final_emit))
+
+
+def _seeds(seeds) -> ctypes.Array:
+    arr = np.asarray(seeds, dtype=np.uint64).reshape(-1)
+    return (ctypes.c_uint64 * len(arr))(*[int(s) for s in arr])
+
+
+def _ptr(t, dtype_size=None, device=True) -> int:
+    if t is None:
+        return None
+    if device and not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    if dtype_size is not None and t.element_size() != dtype_size:
+        raise ValueError(f"expected {dtype_size}-byte elements, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream_handle(stream) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+class Context:
+    """Shapes, per-canvas bounds, caller-owned scratch and state, optional outputs.
+
+    Owns torch device tensors: ``workspace`` (uint8), ``state`` (int32 words, see
+    ``state_views``) and the optional per-step outputs.
+    """
+
+    def __init__(self, B, L, V, d, G, bounds, device="cuda", outputs=True, logits=False,
+                 commit_trace=False):
+        import torch
+        lib = load_library()
+        self.B, self.L, self.V, self.d, self.G = int(B), int(L), int(V), int(d), int(G)
+        b = np.asarray(bounds, dtype=np.float32).reshape(-1)
+        if b.shape[0] != self.B:
+            raise ValueError("need one entropy bound per canvas")
+        self._bounds = (ctypes.c_float * self.B)(*[float(x) for x in b])
+        ws = lib.dgd_workspace_bytes(self.B, self.L, self.V, self.d)
+        if ws == 0:
+            raise ValueError(f"unsupported shape B={B} L={L} V={V} d={d}")
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=device)
+        sb = lib.dgd_state_bytes(self.B, self.L)
+        self.state = torch.zeros(sb // 4, dtype=torch.int32, device=device)
+        BL = self.B * self.L
+        self.entropy = torch.empty(BL, dtype=torch.float32, device=device) if outputs else None
+        self.argmax = torch.empty(BL, dtype=torch.int32, device=device) if outputs else None
+        self.token = torch.empty(BL, dtype=torch.int32, device=device) if outputs else None
+        self.gap = torch.empty(BL, dtype=torch.float32, device=device) if outputs else None
+        self.logits = (torch.empty(BL * self.V, dtype=torch.float32, device=device)
+                       if logits else None)
+        self.commit_step = (torch.full((self.B * self.G,), -1, dtype=torch.int16, device=device)
+                            if commit_trace else None)
+        self._k1_ms = ctypes.c_double(0.0)
+        self._k1_n = ctypes.c_int32(0)
+        self.time_k1 = False
+
+    def state_views(self) -> dict:
+        B, BL = self.B, self.B * self.L
+        s = self.state
+        return {
+            "prev_argmax": s[:BL],
+            "stable_count": s[BL:BL + B],
+            "done": s[BL + B:BL + 2 * B],
+            "steps_used": s[BL + 2 * B:BL + 3 * B],
+            "converged": s[BL + 3 * B:BL + 4 * B],
+            "n_committed": s[BL + 4 * B:BL + 5 * B],
+            "mean_entropy": s[BL + 5 * B:BL + 6 * B].view(__import__("torch").float32),
+            "new_commits": s[BL + 6 * B:BL + 7 * B],
+        }
+
+    def k1_time(self):
+        """(summed projection-kernel ms, launches) of the last timed call."""
+        return self._k1_ms.value, self._k1_n.value
+
+    def as_ctypes(self, stream=None) -> DgdCtx:
+        c = DgdCtx()
+        c.B, c.L, c.V, c.d, c.G = self.B, self.L, self.V, self.d, self.G
+        c.entropy_bound = self._bounds
+        c.workspace = _ptr(self.workspace)
+        c.workspace_bytes = self.workspace.numel()
+        c.state = _ptr(self.state)
+        c.stream = _stream_handle(stream)
+        c.entropy = _ptr(self.entropy)
+        c.argmax = _ptr(self.argmax)
+        c.token = _ptr(self.token)
+        c.gap = _ptr(self.gap)
+        c.logits = _ptr(self.logits)
+        c.commit_step = _ptr(self.commit_step)
+        if self.time_k1:
+            c.k1_ms = ctypes.pointer(self._k1_ms)
+            c.k1_launches = ctypes.pointer(self._k1_n)
+        return c
+
+
+# ----------------------------------------------------------------------------
+# C entry points
+# ----------------------------------------------------------------------------
+def dgd_state_bytes(B: int, L: int) -> int:
+    return int(load_library().dgd_state_bytes(B, L))
+
+
+def dgd_workspace_bytes(B: int, L: int, V: int, d: int) -> int:
+    return int(load_library().dgd_workspace_bytes(B, L, V, d))
+
+
+def dgd_last_error() -> str:
+    return load_library().dgd_last_error().decode()
+
+
+def dgd_init_block(canvas, committed, block, params: DgdParams, seeds, ctx: Context, stream=None):
+    c = ctx.as_ctypes(stream)
+    _check(load_library().dgd_init_block(_ptr(canvas, 4), _ptr(committed, 1), int(block),
+                                         ctypes.byref(params), _seeds(seeds), ctypes.byref(c)))
+
+
+def dgd_step(H, W_vocab, canvas, committed, block, step, params: DgdParams, seeds, ctx: Context,
+             stream=None):
+    c = ctx.as_ctypes(stream)
+    _check(load_library().dgd_step(_ptr(H, 2), _ptr(W_vocab, 2), _ptr(canvas, 4),
+                                   _ptr(committed, 1), int(block), int(step),
+                                   ctypes.byref(params), _seeds(seeds), ctypes.byref(c)))
+
+
+def dgd_run(H_steps, W_vocab, canvas, committed, params: DgdParams, seeds, ctx: Context,
+            stream=None):
+    c = ctx.as_ctypes(stream)
+    _check(load_library().dgd_run(_ptr(H_steps, 2), _ptr(W_vocab, 2), _ptr(canvas, 4),
+                                  _ptr(committed, 1), ctypes.byref(params), _seeds(seeds),
+                                  ctypes.byref(c)))
+
+
+def dgd_debug_gumbel(words, out, stream=None):
+    _check(load_library().dgd_debug_gumbel(_ptr(words, 4), _ptr(out, 4), int(words.numel()),
+                                           _stream_handle(stream)))
