@@ -94,14 +94,20 @@ def temperature(step: int, N: int, t_min: float, t_max: float) -> float:
 # ----------------------------------------------------------------------------
 # 2. logits
 # ----------------------------------------------------------------------------
-def projection(H_bits: np.ndarray, W_bits: np.ndarray, v_chunk: int = 16384) -> np.ndarray:
-    """z[r, v] = sum_k H[r, k] W[v, k] in float64 (products of bf16 are exact)."""
+def projection(H_bits: np.ndarray, W_bits: np.ndarray, v_chunk: int = 16384,
+               W64: np.ndarray = None) -> np.ndarray:
+    """z[r, v] = sum_k H[r, k] W[v, k] in float64 (products of bf16 are exact).
+
+    ``W64`` may carry W already widened to float64 (same values) to avoid
+    re-widening the table on every call.
+    """
     H = bf16_to_f64(H_bits)
     rows, V = H.shape[0], W_bits.shape[0]
     z = np.empty((rows, V), dtype=np.float64)
     for v0 in range(0, V, v_chunk):
         v1 = min(V, v0 + v_chunk)
-        z[:, v0:v1] = H @ bf16_to_f64(W_bits[v0:v1]).T
+        Wc = W64[v0:v1] if W64 is not None else bf16_to_f64(W_bits[v0:v1])
+        z[:, v0:v1] = H @ Wc.T
     return z
 
 
@@ -348,14 +354,14 @@ def step_from_stats(state: CanvasState, stats: dict, block: int, step: int, L: i
 
 
 def step(state: CanvasState, H_bits: np.ndarray, W_bits: np.ndarray, block: int, step_idx: int,
-         params: Params, seed: int, bound: float):
+         params: Params, seed: int, bound: float, W64: np.ndarray = None):
     """One denoising step of one canvas: H_bits [L, d] bf16 bits, W_bits [V, d]."""
     L = H_bits.shape[0]
     V = W_bits.shape[0]
     if state.done:
         return state.copy(), {"skipped": True}
     T = temperature(step_idx, params.N, params.t_min, params.t_max)
-    z = projection(H_bits, W_bits)
+    z = projection(H_bits, W_bits, W64=W64)
     stats = position_stats(z, T, seed, block * L + np.arange(L), block * params.N + step_idx)
     new, info = step_from_stats(state, stats, block, step_idx, L, V, params, seed, bound)
     info["T"] = T
