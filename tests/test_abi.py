@@ -37,10 +37,10 @@ def test_state_and_workspace_sizes(lib):
     assert dgd.dgd_state_bytes(1, 256) == (256 + 7) * 4
     assert dgd.dgd_state_bytes(8, 256) == (8 * 256 + 56) * 4
     assert dgd.dgd_state_bytes(0, 16) == 0
-    # 256 positions x 512 vocabulary groups x 32-byte records dominate
+    # 256 positions x 256 vocabulary groups x 32-byte records dominate
     ws = dgd.dgd_workspace_bytes(1, 256, 262144, 2816)
-    assert 256 * 512 * 32 <= ws <= 256 * 512 * 32 + 8192
-    assert dgd.dgd_workspace_bytes(1, 16, 1024, 64) >= 16 * 8 * 32
+    assert 256 * 256 * 32 <= ws <= 256 * 256 * 32 + 8192
+    assert dgd.dgd_workspace_bytes(1, 16, 1024, 64) >= 16 * 4 * 32   # V=1024: 4 groups
     for bad in [(0, 16, 1024, 64), (65, 16, 1024, 64), (1, 4097, 1024, 64), (1, 16, 0, 64),
                 (1, 16, 1024, 60), (1, 16, 1024, 0), (1, 16, (1 << 24) + 1, 64)]:
         assert dgd.dgd_workspace_bytes(*bad) == 0, bad

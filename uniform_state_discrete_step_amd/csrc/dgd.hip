@@ -39,10 +39,11 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 256;           // 4 waves of 64
 constexpr int kWaves = kThreads / 64;
-constexpr int kVocabPerWave = 32;       // MFMA A rows (vocabulary) per wave
-constexpr int kVocabTile = kWaves * kVocabPerWave;   // 128 vocabulary rows per tile
+constexpr int kVB = 2;                  // 32-row vocabulary blocks per wave (A fragments)
+constexpr int kVocabPerWave = 32 * kVB; // 64 vocabulary rows per wave
+constexpr int kVocabTile = kWaves * kVocabPerWave;   // 256 vocabulary rows per tile
 constexpr int kKChunk = 64;             // hidden elements per LDS stage
-constexpr int kMaxGroups = 512;         // vocabulary groups (partials per position)
+constexpr int kMaxGroups = 256;         // vocabulary groups (partials per position)
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
@@ -134,31 +135,45 @@ __device__ inline void tile_of_block(int id, int n_mtiles, int P, int& mt, int& 
 
 __device__ inline bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// Raw buffer resources: word 3 selects 32-bit untyped access on gfx9-family
+// parts; kOOB is an offset beyond any num_records (the load returns zero).
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kNonTemporal = 2;   // streaming (nt) cache policy for W
+
 // ---------------------------------------------------------------------------
 // k_project: fused projection + tempered softmax-entropy / argmax / Gumbel-max
 // ---------------------------------------------------------------------------
-// Workgroup = 4 waves; tile = 128 vocabulary rows (32 per wave) x MROWS = 32*MB
-// positions.  MFMA v_mfma_f32_32x32x16_bf16 with A = W (vocabulary along the
-// MFMA rows) and B = H (positions along the MFMA columns), so lane l of a
-// wave holds, per 32-position block, 16 logits of ONE position (column l%32)
-// at vocabulary rows 8q + 4(l/32) + e (q, e = 0..3): four groups of four
-// consecutive vocabulary ids, i.e. exactly the four words of one Philox call.
+// Workgroup = 4 waves, one per SIMD; tile = 256 vocabulary rows (64 per wave,
+// two 32-row blocks) x MROWS = 32*MB positions.  MFMA
+// v_mfma_f32_32x32x16_bf16 with A = W (vocabulary along the MFMA rows) and
+// B = H (positions along the MFMA columns): every H fragment read from LDS
+// feeds two MFMAs, and lane l of a wave holds, per 32-position block and per
+// vocabulary block, 16 logits of ONE position (column l%32) at vocabulary
+// rows 8q + 4(l/32) + e (q, e = 0..3): groups of four consecutive ids, i.e.
+// exactly the four words of one Philox call.
 //
-// K loop: per 64-element hidden chunk each lane loads the 64 contiguous
-// bytes W[v][32h .. 32h+31] (h = lane/32) and the workgroup stages the
-// [MROWS x 64] H chunk in LDS (double buffered, 16-byte segments XOR-swizzled
-// by row).  MFMA sub-step s (0..3) uses hidden elements 32h + 8s .. +7 for
-// lane half h in both operands: the same permutation of k on A and B, so the
-// products summed are exactly those of the plain dot product.
-template <int MB, bool kLogits>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(MB >= 8 ? 1 : 2)))
+// K loop: per 64-element hidden chunk each lane loads, for its two vocabulary
+// rows, the 64 contiguous bytes W[v][32h .. 32h+31] (h = lane/32), kWDepth
+// chunks deep in registers; the workgroup stages the [MROWS x 64] H chunk in
+// LDS (double buffered, 16-byte segments XOR-swizzled by row).  MFMA
+// sub-step s (0..3) uses hidden elements 32h + 8s .. +7 for lane half h in
+// both operands: the same permutation of k on A and B, so the products summed
+// are exactly those of the plain dot product.
+//
+// kUniformKey: every 32-row block lies inside one canvas (L % 32 == 0), so the
+// Philox key is wave-uniform and lives in scalar registers.
+template <int MB, bool kLogits, bool kUniformKey>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_project(const ProjArgs a) {
   constexpr int MROWS = 32 * MB;
   constexpr int HSEG = MROWS * (kKChunk / 8) / kThreads;   // 16-byte H segments per thread
-  constexpr int NREC = MB >= 2 ? MB / 2 : 1;
+  constexpr int WSEG = kVB * 4;                             // 16-byte W segments per lane per chunk
   static_assert(HSEG >= 1, "tile too small");
-  static_assert(kWaves * MROWS * (int)sizeof(Rec) <= 2 * MROWS * kKChunk * 2, "LDS reuse");
+  static_assert(MB == 1 || MB == 2 || MB == 4 || MB == 8, "MB");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * MROWS * kKChunk * 2];
+  // running record of every (wave, position) over the tiles seen so far
+  __shared__ __attribute__((aligned(16))) Rec recs[kWaves * MROWS];
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
@@ -175,40 +190,52 @@ k_project(const ProjArgs a) {
     if (all_done) return;
   }
 
-  Rec run[NREC];
-#pragma unroll
-  for (int i = 0; i < NREC; ++i) run[i] = rec_empty();
+  for (int i = tid; i < kWaves * MROWS; i += kThreads) rec_store(recs + i, rec_empty());
+  // (the first __syncthreads of the tile loop orders these writes)
 
   const int nk = (a.d + kKChunk - 1) / kKChunk;
   const size_t d = (size_t)a.d;
 
   for (int vt = g; vt < a.n_vtiles; vt += a.P) {
     const int vbase = vt * kVocabTile + wave * kVocabPerWave;
-    const int vlane = vbase + col;
-    const bool wvalid = vlane < a.V;
-    const uint16_t* wrow = a.W + (size_t)(wvalid ? vlane : 0) * d;
-
-    auto load_w = [&](int c, u32x4_t (&dst)[4]) {
+    // Buffer resources for this tile: rows past the end of W (or of the
+    // M tile) lie beyond num_records and read as zero without a memory
+    // access; so does any offset set to kOOB.  All offsets are in the
+    // 32-bit VGPR offset so the range check covers them.
+    const int vrows = min(kVocabTile, a.V - vt * kVocabTile);
+    const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.W + (size_t)vt * kVocabTile * d), (short)0, (int)((size_t)vrows * d * 2), kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.H + (size_t)row0 * d), (short)0, (int)((size_t)min(MROWS, a.M - row0) * d * 2),
+        kRsrcWord3);
+    uint32_t woff[kVB];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int kel = c * kKChunk + 32 * half + 8 * s;
-        if (wvalid && kel < a.d)
-          dst[s] = __builtin_nontemporal_load((const u32x4_t*)(wrow + kel));
-        else
-          dst[s] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+    for (int vb = 0; vb < kVB; ++vb)
+      woff[vb] = (uint32_t)((wave * kVocabPerWave + vb * 32 + col) * d * 2 + half * 64);
+    const uint32_t hoff = (uint32_t)((tid >> 3) * d * 2 + (tid & 7) * 16);
+    const uint32_t hstride = (uint32_t)(32 * d * 2);   // 32 rows
+
+    // Loads of hidden elements past d (including whole chunks past the end)
+    // get bit 31 set in their offset: beyond num_records, they read zeros
+    // without a memory access.  Built with bit operations, not a select, so
+    // the loop body stays straight-line code.
+    auto load_w = [&](int c, u32x4_t (&dst)[WSEG]) {
+      const int kbase = c * kKChunk + 32 * half;
+#pragma unroll
+      for (int vb = 0; vb < kVB; ++vb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t oob = (uint32_t)(kbase + 8 * s >= a.d) << 31;
+          const uint32_t off = (woff[vb] + (uint32_t)(c * kKChunk * 2 + s * 16)) | oob;
+          dst[vb * 4 + s] = __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, kNonTemporal);
+        }
     };
     auto load_h = [&](int c, u32x4_t (&dst)[HSEG]) {
+      const uint32_t oob = (uint32_t)(c * kKChunk + (tid & 7) * 8 >= a.d) << 31;
 #pragma unroll
       for (int i = 0; i < HSEG; ++i) {
-        const int idx = i * kThreads + tid;
-        const int r = idx >> 3, e = idx & 7;
-        const int grow = row0 + r;
-        const int kel = c * kKChunk + e * 8;
-        if (grow < a.M && kel < a.d)
-          dst[i] = *(const u32x4_t*)(a.H + (size_t)grow * d + kel);
-        else
-          dst[i] = u32x4_t{0u, 0u, 0u, 0u};
+        const uint32_t off = (hoff + (uint32_t)i * hstride + (uint32_t)(c * kKChunk * 2)) | oob;
+        dst[i] = __builtin_amdgcn_raw_buffer_load_b128(hres, off, 0, 0);
       }
     };
     auto store_h = [&](int buf, const u32x4_t (&src)[HSEG]) {
@@ -221,84 +248,116 @@ k_project(const ProjArgs a) {
       }
     };
 
-    f32x16_t acc[MB];
+    f32x16_t acc[kVB][MB];
 #pragma unroll
-    for (int pb = 0; pb < MB; ++pb)
+    for (int vb = 0; vb < kVB; ++vb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[pb][i] = 0.f;
+      for (int pb = 0; pb < MB; ++pb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[vb][pb][i] = 0.f;
 
-    u32x4_t wc[4], wn[4], hs[HSEG];
-    __syncthreads();   // previous tile's readers of smem are done
-    load_w(0, wc);
-    load_h(0, hs);
-    store_h(0, hs);
-    __syncthreads();
-
-    for (int c = 0; c < nk; ++c) {
-      const int buf = c & 1;
-      const bool more = c + 1 < nk;
-      if (more) {
-        load_h(c + 1, hs);
-        load_w(c + 1, wn);
-      }
-      const uint8_t* hb = smem + buf * (MROWS * kKChunk * 2);
+    // One chunk: MFMAs on W chunk `wc` and the H chunk in LDS buffer c&1,
+    // with the next H chunk (L2-resident, one ahead) and the W chunk two
+    // ahead (HBM) in flight.  Chunks past the end read zeros: their MFMAs
+    // add exact zeros, so the loop runs whole rounds of kRing chunks and the
+    // ring index stays static (no register copies that would wait on loads).
+    // Issue order is pinned (vmcnt retires loads in order): H(c+1) strictly
+    // before W(c+2), so waiting for H at the end of the chunk does not drain
+    // the W prefetch.
+    auto chunk = [&](int c, const u32x4_t (&wc)[WSEG], u32x4_t (&wnext2)[WSEG], u32x4_t (&hs)[HSEG]) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_h(c + 1, hs);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(c + 2, wnext2);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* hb = smem + (c & 1) * (MROWS * kKChunk * 2);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bf16x8_t av = as_bf16x8(wc[s]);
 #pragma unroll
         for (int pb = 0; pb < MB; ++pb) {
           const int r = pb * 32 + col;
           const int e = (4 * half + s) ^ (col & 7);
-          const u32x4_t bv = *(const u32x4_t*)(hb + r * 128 + (e << 4));
-          acc[pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, as_bf16x8(bv), acc[pb], 0, 0, 0);
+          const bf16x8_t bv = as_bf16x8(*(const u32x4_t*)(hb + r * 128 + (e << 4)));
+#pragma unroll
+          for (int vb = 0; vb < kVB; ++vb)
+            acc[vb][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                as_bf16x8(wc[vb * 4 + s]), bv, acc[vb][pb], 0, 0, 0);
         }
       }
-      if (more) {
-        store_h(buf ^ 1, hs);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) wc[s] = wn[s];
-      }
+      store_h((c + 1) & 1, hs);
       __syncthreads();
+    };
+
+    u32x4_t w0[WSEG], w1[WSEG], w2[WSEG], hs[HSEG];
+    __syncthreads();   // previous tile's readers of smem are done
+    load_w(0, w0);
+    load_w(1, w1);
+    load_h(0, hs);
+    store_h(0, hs);
+    __syncthreads();
+    for (int c = 0; c < nk; c += 3) {
+      chunk(c, w0, w2, hs);
+      chunk(c + 1, w1, w0, hs);
+      chunk(c + 2, w2, w1, hs);
     }
 
     // ---------------- epilogue: one position per lane per block ----------
-#pragma unroll
+    // One loop body for all blocks (not unrolled: it is long); the switch
+    // keeps every accumulator index static so the tile stays in registers.
+#pragma unroll 1
     for (int pb = 0; pb < MB; ++pb) {
+      f32x16_t z[kVB];
+      switch (pb) {
+#define DGD_TAKE(P)                                            \
+  case P:                                                      \
+    _Pragma("unroll") for (int vb = 0; vb < kVB; ++vb)         \
+        z[vb] = acc[vb][(P) < MB ? (P) : 0];                   \
+    break;
+        DGD_TAKE(0) DGD_TAKE(1) DGD_TAKE(2) DGD_TAKE(3)
+        DGD_TAKE(4) DGD_TAKE(5) DGD_TAKE(6) DGD_TAKE(7)
+#undef DGD_TAKE
+      }
       const int r = row0 + pb * 32 + col;
       const bool rvalid = r < a.M;
-      const int cv = rvalid ? r / a.L : 0;
+      int cv = rvalid ? r / a.L : 0;
+      if constexpr (kUniformKey) cv = __builtin_amdgcn_readfirstlane(cv);
       const int p = r - cv * a.L;
       const uint32_t pabs = (uint32_t)(a.block * a.L + p);
       const uint32_t key0 = a.key[cv][0], key1 = a.key[cv][1];
 
-      float x[16];
+      float x[kVB * 16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = acc[pb][i] * a.c2;
+      for (int vb = 0; vb < kVB; ++vb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) x[vb * 16 + i] = z[vb][i] * a.c2;
 
       if constexpr (kLogits) {
         if (rvalid) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int v0 = vbase + 8 * q + 4 * half;
-            float* dst = a.logits + (size_t)r * a.V + v0;
+          for (int vb = 0; vb < kVB; ++vb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (v0 + e < a.V) dst[e] = acc[pb][4 * q + e];
-          }
+            for (int q = 0; q < 4; ++q) {
+              const int v0 = vbase + vb * 32 + 8 * q + 4 * half;
+              float* dst = a.logits + (size_t)r * a.V + v0;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (v0 + e < a.V) dst[e] = z[vb][4 * q + e];
+            }
         }
       }
 
+      // value index i = vb*16 + 4q + e  <->  vocabulary id vbase + vb*32 + 8q + 4h + e
       float m = kNeg;
       int am = kNoIndex;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = vbase + 8 * (i >> 2) + 4 * half + (i & 3);
+      for (int i = 0; i < kVB * 16; ++i) {
+        const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
         if (v < a.V && x[i] > m) { m = x[i]; am = v; }
       }
       float S = 0.f, A = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int v = vbase + 8 * (i >> 2) + 4 * half + (i & 3);
+      for (int i = 0; i < kVB * 16; ++i) {
+        const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
         if (v < a.V) {
           const float dx = x[i] - m;
           const float e = fexp2(dx);
@@ -309,14 +368,14 @@ k_project(const ProjArgs a) {
       float y1 = kNeg, y2 = kNeg;
       int i1 = kNoIndex;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int v0 = vbase + 8 * q + 4 * half;
+      for (int grp = 0; grp < kVB * 4; ++grp) {
+        const int v0 = vbase + (grp >> 2) * 32 + 8 * (grp & 3) + 4 * half;
         const Philox4 pw = philox4x32_10((uint32_t)v0 >> 2, pabs, (uint32_t)a.gstep, 0u, key0, key1);
         const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           if (v0 + e < a.V) {
-            const float y = x[4 * q + e] + gumbel_bits(words[e]);
+            const float y = x[4 * grp + e] + gumbel_bits(words[e]);
             if (y > y1) { y2 = y1; y1 = y; i1 = v0 + e; }
             else if (y > y2) { y2 = y; }
           }
@@ -327,27 +386,19 @@ k_project(const ProjArgs a) {
       loc.y1 = y1; loc.i1 = i1; loc.y2 = y2; loc.pad = 0.f;
       const Rec oth = rec_shfl_xor(loc, 32);
       const Rec wrec = rec_merge(rec_pick(half == 0, loc, oth), rec_pick(half == 0, oth, loc));
-      if constexpr (MB == 1) {
-        if (half == 0) run[0] = rec_merge(run[0], wrec);
-      } else {
-        if (half == (pb & 1)) run[pb >> 1] = rec_merge(run[pb >> 1], wrec);
+      if (half == 0) {
+        Rec* slot = recs + wave * MROWS + pb * 32 + col;
+        rec_store(slot, rec_merge(rec_load(slot), wrec));
       }
     }
   }
 
   // ---------------- merge the four waves (fixed order) and write ----------
   __syncthreads();
-  Rec* rl = reinterpret_cast<Rec*>(smem);
-#pragma unroll
-  for (int pb = 0; pb < MB; ++pb) {
-    const bool own = (MB == 1) ? (half == 0) : (half == (pb & 1));
-    if (own) rec_store(rl + wave * MROWS + pb * 32 + col, run[MB == 1 ? 0 : (pb >> 1)]);
-  }
-  __syncthreads();
   for (int t = tid; t < MROWS; t += kThreads) {
-    Rec r = rec_load(rl + t);
+    Rec r = rec_load(recs + t);
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = rec_merge(r, rec_load(rl + w * MROWS + t));
+    for (int w = 1; w < kWaves; ++w) r = rec_merge(r, rec_load(recs + w * MROWS + t));
     const int row = row0 + t;
     if (row < a.M) rec_store(a.part + (size_t)row * a.P + g, r);
   }
@@ -761,11 +812,14 @@ struct Timer {
 };
 
 template <int MB>
-void launch_project_mb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits) {
-  if (logits)
-    hipLaunchKernelGGL((k_project<MB, true>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_project<MB, false>), grid, dim3(kThreads), 0, s, a);
+void launch_project_mb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits, bool uniform) {
+  if (logits) {
+    if (uniform) hipLaunchKernelGGL((k_project<MB, true, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_project<MB, true, false>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (uniform) hipLaunchKernelGGL((k_project<MB, false, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_project<MB, false, false>), grid, dim3(kThreads), 0, s, a);
+  }
 }
 
 int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* committed,
@@ -799,11 +853,12 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   int rc = timer.begin(stream);
   if (rc) return rc;
   const bool lg = ctx->logits != nullptr;
+  const bool uni = (L % 32) == 0;
   switch (MB) {
-    case 1: launch_project_mb<1>(pa, grid1, stream, lg); break;
-    case 2: launch_project_mb<2>(pa, grid1, stream, lg); break;
-    case 4: launch_project_mb<4>(pa, grid1, stream, lg); break;
-    default: launch_project_mb<8>(pa, grid1, stream, lg); break;
+    case 1: launch_project_mb<1>(pa, grid1, stream, lg, uni); break;
+    case 2: launch_project_mb<2>(pa, grid1, stream, lg, uni); break;
+    case 4: launch_project_mb<4>(pa, grid1, stream, lg, uni); break;
+    default: launch_project_mb<8>(pa, grid1, stream, lg, uni); break;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "k_project launch");
