@@ -135,6 +135,13 @@ __device__ inline void tile_of_block(int id, int n_mtiles, int P, int& mt, int& 
 
 __device__ inline bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// LDS rows are 128 bytes (eight 16-byte segments); segment e of row r is
+// stored in slot e ^ swz(r).  swz differs for the 8 rows of any aligned
+// group of 8, and for the 8 even (and the 8 odd) rows of any aligned group of
+// 16, so 128-bit accesses by consecutive lanes to consecutive rows are
+// conflict-free whether the LDS serves 8 or 16 such lanes per cycle.
+__device__ inline int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 // Raw buffer resources: word 3 selects 32-bit untyped access on gfx9-family
 // parts; kOOB is an offset beyond any num_records (the load returns zero).
 constexpr int kRsrcWord3 = 0x00020000;
@@ -168,12 +175,17 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
 k_project(const ProjArgs a) {
   constexpr int MROWS = 32 * MB;
   constexpr int HSEG = MROWS * (kKChunk / 8) / kThreads;   // 16-byte H segments per thread
-  constexpr int WSEG = kVB * 4;                             // 16-byte W segments per lane per chunk
   static_assert(HSEG >= 1, "tile too small");
   static_assert(MB == 1 || MB == 2 || MB == 4 || MB == 8, "MB");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * MROWS * kKChunk * 2];
+  // LDS: H chunk [MROWS x 64] and W chunk [256 x 64] bf16, double buffered,
+  // 16-byte segments XOR-swizzled by row; then the running records.
+  constexpr int HBUF = MROWS * kKChunk * 2;
+  constexpr int WBUF = kVocabTile * kKChunk * 2;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * HBUF + 2 * WBUF];
   // running record of every (wave, position) over the tiles seen so far
   __shared__ __attribute__((aligned(16))) Rec recs[kWaves * MROWS];
+  uint8_t* const hbuf0 = smem;
+  uint8_t* const wbuf0 = smem + 2 * HBUF;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
@@ -208,10 +220,11 @@ k_project(const ProjArgs a) {
     const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.H + (size_t)row0 * d), (short)0, (int)((size_t)min(MROWS, a.M - row0) * d * 2),
         kRsrcWord3);
-    uint32_t woff[kVB];
-#pragma unroll
-    for (int vb = 0; vb < kVB; ++vb)
-      woff[vb] = (uint32_t)((wave * kVocabPerWave + vb * 32 + col) * d * 2 + half * 64);
+    // W rows of this wave are loaded fully coalesced: instruction j covers
+    // rows 8j .. 8j+7 of the wave's 64, lane l reading 16 bytes at segment
+    // l%8 of row l/8 (eight lanes per 128-byte line).
+    const uint32_t woff = (uint32_t)((wave * kVocabPerWave + (lane >> 3)) * d * 2 + (lane & 7) * 16);
+    const uint32_t wstride = (uint32_t)(8 * d * 2);    // 8 rows
     const uint32_t hoff = (uint32_t)((tid >> 3) * d * 2 + (tid & 7) * 16);
     const uint32_t hstride = (uint32_t)(32 * d * 2);   // 32 rows
 
@@ -219,16 +232,21 @@ k_project(const ProjArgs a) {
     // get bit 31 set in their offset: beyond num_records, they read zeros
     // without a memory access.  Built with bit operations, not a select, so
     // the loop body stays straight-line code.
-    auto load_w = [&](int c, u32x4_t (&dst)[WSEG]) {
-      const int kbase = c * kKChunk + 32 * half;
+    auto load_w = [&](int c, u32x4_t (&dst)[8]) {
+      const uint32_t oob = (uint32_t)(c * kKChunk + (lane & 7) * 8 >= a.d) << 31;
 #pragma unroll
-      for (int vb = 0; vb < kVB; ++vb)
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t off = (woff + (uint32_t)j * wstride + (uint32_t)(c * kKChunk * 2)) | oob;
+        dst[j] = __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, kNonTemporal);
+      }
+    };
+    auto store_w = [&](int buf, const u32x4_t (&src)[8]) {
+      uint8_t* base = wbuf0 + buf * WBUF;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const uint32_t oob = (uint32_t)(kbase + 8 * s >= a.d) << 31;
-          const uint32_t off = (woff[vb] + (uint32_t)(c * kKChunk * 2 + s * 16)) | oob;
-          dst[vb * 4 + s] = __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, kNonTemporal);
-        }
+      for (int j = 0; j < 8; ++j) {
+        const int r = wave * kVocabPerWave + 8 * j + (lane >> 3);
+        *(u32x4_t*)(base + r * 128 + (((lane & 7) ^ swz(r)) << 4)) = src[j];
+      }
     };
     auto load_h = [&](int c, u32x4_t (&dst)[HSEG]) {
       const uint32_t oob = (uint32_t)(c * kKChunk + (tid & 7) * 8 >= a.d) << 31;
@@ -239,12 +257,12 @@ k_project(const ProjArgs a) {
       }
     };
     auto store_h = [&](int buf, const u32x4_t (&src)[HSEG]) {
-      uint8_t* base = smem + buf * (MROWS * kKChunk * 2);
+      uint8_t* base = hbuf0 + buf * HBUF;
 #pragma unroll
       for (int i = 0; i < HSEG; ++i) {
         const int idx = i * kThreads + tid;
         const int r = idx >> 3, e = idx & 7;
-        *(u32x4_t*)(base + r * 128 + ((e ^ (r & 7)) << 4)) = src[i];
+        *(u32x4_t*)(base + r * 128 + ((e ^ swz(r)) << 4)) = src[i];
       }
     };
 
@@ -256,49 +274,52 @@ k_project(const ProjArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[vb][pb][i] = 0.f;
 
-    // One chunk: MFMAs on W chunk `wc` and the H chunk in LDS buffer c&1,
-    // with the next H chunk (L2-resident, one ahead) and the W chunk two
-    // ahead (HBM) in flight.  Chunks past the end read zeros: their MFMAs
-    // add exact zeros, so the loop runs whole rounds of kRing chunks and the
-    // ring index stays static (no register copies that would wait on loads).
-    // Issue order is pinned (vmcnt retires loads in order): H(c+1) strictly
-    // before W(c+2), so waiting for H at the end of the chunk does not drain
-    // the W prefetch.
-    auto chunk = [&](int c, const u32x4_t (&wc)[WSEG], u32x4_t (&wnext2)[WSEG], u32x4_t (&hs)[HSEG]) {
+    // One chunk: MFMAs on the W and H chunks in LDS buffer c&1 while H(c+1)
+    // (L2-resident) and W(c+2) (HBM) are in flight; W(c+1), loaded one chunk
+    // earlier, is written to LDS at the end.  The issue order is pinned
+    // (vmcnt retires loads in order): H(c+1) strictly before W(c+2), so the
+    // wait for H at the end of the chunk leaves the W prefetch in flight.
+    // Chunks past the end read zeros and add exact zeros, so the loop runs
+    // whole pairs of chunks and the register ring index stays static.
+    auto chunk = [&](int c, u32x4_t (&wload)[8], const u32x4_t (&wstore)[8], u32x4_t (&hs)[HSEG]) {
       __builtin_amdgcn_sched_barrier(0);
       load_h(c + 1, hs);
       __builtin_amdgcn_sched_barrier(0);
-      load_w(c + 2, wnext2);
+      load_w(c + 2, wload);
       __builtin_amdgcn_sched_barrier(0);
-      const uint8_t* hb = smem + (c & 1) * (MROWS * kKChunk * 2);
+      const uint8_t* hb = hbuf0 + (c & 1) * HBUF;
+      const uint8_t* wb = wbuf0 + (c & 1) * WBUF;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        const int e = (4 * half + s) ^ swz(col);
+        bf16x8_t av[kVB];
+#pragma unroll
+        for (int vb = 0; vb < kVB; ++vb)
+          av[vb] = as_bf16x8(*(const u32x4_t*)(wb + (wave * kVocabPerWave + vb * 32 + col) * 128 + (e << 4)));
 #pragma unroll
         for (int pb = 0; pb < MB; ++pb) {
-          const int r = pb * 32 + col;
-          const int e = (4 * half + s) ^ (col & 7);
-          const bf16x8_t bv = as_bf16x8(*(const u32x4_t*)(hb + r * 128 + (e << 4)));
+          const bf16x8_t bv = as_bf16x8(*(const u32x4_t*)(hb + (pb * 32 + col) * 128 + (e << 4)));
 #pragma unroll
           for (int vb = 0; vb < kVB; ++vb)
-            acc[vb][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                as_bf16x8(wc[vb * 4 + s]), bv, acc[vb][pb], 0, 0, 0);
+            acc[vb][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[vb], bv, acc[vb][pb], 0, 0, 0);
         }
       }
       store_h((c + 1) & 1, hs);
+      store_w((c + 1) & 1, wstore);
       __syncthreads();
     };
 
-    u32x4_t w0[WSEG], w1[WSEG], w2[WSEG], hs[HSEG];
+    u32x4_t wx[8], wy[8], hs[HSEG];
     __syncthreads();   // previous tile's readers of smem are done
-    load_w(0, w0);
-    load_w(1, w1);
+    load_w(0, wx);
+    load_w(1, wy);
     load_h(0, hs);
+    store_w(0, wx);
     store_h(0, hs);
     __syncthreads();
-    for (int c = 0; c < nk; c += 3) {
-      chunk(c, w0, w2, hs);
-      chunk(c + 1, w1, w0, hs);
-      chunk(c + 2, w2, w1, hs);
+    for (int c = 0; c < nk; c += 2) {
+      chunk(c, wx, wy, hs);       // loads W(c+2) into wx, stores W(c+1) from wy
+      chunk(c + 1, wy, wx, hs);   // loads W(c+3) into wy, stores W(c+2) from wx
     }
 
     // ---------------- epilogue: one position per lane per block ----------
@@ -346,24 +367,31 @@ k_project(const ProjArgs a) {
         }
       }
 
-      // value index i = vb*16 + 4q + e  <->  vocabulary id vbase + vb*32 + 8q + 4h + e
+      // value index i = vb*16 + 4q + e  <->  vocabulary id vbase + vb*32 + 8q + 4h + e.
+      // In a ragged last tile, ids past V get the sentinel logit kNeg: they
+      // add exact zeros to S and A and never win the argmax or the sample.
+      if (vbase + kVocabPerWave > a.V) {
+#pragma unroll
+        for (int i = 0; i < kVB * 16; ++i) {
+          const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
+          x[i] = v < a.V ? x[i] : kNeg;
+        }
+      }
       float m = kNeg;
       int am = kNoIndex;
 #pragma unroll
-      for (int i = 0; i < kVB * 16; ++i) {
+      for (int i = 0; i < kVB * 16; ++i) {   // first maximum (ids increase with i)
         const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
-        if (v < a.V && x[i] > m) { m = x[i]; am = v; }
+        am = x[i] > m ? v : am;
+        m = fmaxf(m, x[i]);
       }
       float S = 0.f, A = 0.f;
 #pragma unroll
       for (int i = 0; i < kVB * 16; ++i) {
-        const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
-        if (v < a.V) {
-          const float dx = x[i] - m;
-          const float e = fexp2(dx);
-          S += e;
-          A += dx * e;
-        }
+        const float dx = x[i] - m;
+        const float e = fexp2(dx);
+        S += e;
+        A = fmaf(dx, e, A);
       }
       float y1 = kNeg, y2 = kNeg;
       int i1 = kNoIndex;
@@ -373,12 +401,11 @@ k_project(const ProjArgs a) {
         const Philox4 pw = philox4x32_10((uint32_t)v0 >> 2, pabs, (uint32_t)a.gstep, 0u, key0, key1);
         const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (v0 + e < a.V) {
-            const float y = x[4 * grp + e] + gumbel_bits(words[e]);
-            if (y > y1) { y2 = y1; y1 = y; i1 = v0 + e; }
-            else if (y > y2) { y2 = y; }
-          }
+        for (int e = 0; e < 4; ++e) {   // top two, first index on ties
+          const float y = x[4 * grp + e] + gumbel_bits(words[e]);
+          y2 = fmaxf(y2, fminf(y, y1));
+          i1 = y > y1 ? v0 + e : i1;
+          y1 = fmaxf(y1, y);
         }
       }
       Rec loc;
