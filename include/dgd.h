@@ -81,7 +81,8 @@ typedef uint16_t dgd_bf16;
 /* Sampler knobs (node page "Inputs"; TensorSharp doc "3. Sampler contract").
  * Ranges are checked on every call:
  *   num_inference_steps  N in [1, 1024]
- *   t_min, t_max         finite, in [0, 1], and every T_s > 0
+ *   t_min, t_max         finite, in [0, 1], and every T_s >= 1e-4 (so that
+ *                        tempered fp32 logits stay finite)
  *   confidence           early-stop mean-entropy threshold in nats, [0, 1]
  *   stability_threshold  consecutive unchanged-argmax steps needed, [0, 1024]
  *   freeze               1: committed positions stay frozen (default);

@@ -73,6 +73,8 @@ def _step(lib, ctx, params=None, seeds=(0,), block=0, step=0, H=FAKE, W=FAKE):
     (dict(t_min=float("nan")), dgd.DGD_EINVAL),
     (dict(t_max=1.5), dgd.DGD_EINVAL),
     (dict(t_min=0.0, t_max=0.0), dgd.DGD_EINVAL),
+    (dict(t_min=1e-5, t_max=1e-5), dgd.DGD_EINVAL),
+    (dict(N=1, t_min=0.0, t_max=5e-5), dgd.DGD_EINVAL),
     (dict(confidence=-0.1), dgd.DGD_EINVAL),
     (dict(stability_threshold=-1), dgd.DGD_EINVAL),
     (dict(freeze=2), dgd.DGD_EINVAL),

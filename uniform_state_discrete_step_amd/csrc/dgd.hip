@@ -37,11 +37,14 @@ namespace {
 // ---------------------------------------------------------------------------
 // tiling constants of the projection
 // ---------------------------------------------------------------------------
-constexpr int kThreads = 256;           // 4 waves of 64
+constexpr int kThreads = 256;           // merge/commit and init kernels: 4 waves of 64
 constexpr int kWaves = kThreads / 64;
+constexpr int kPThreads = 512;          // projection: 8 waves, two per SIMD
+constexpr int kVGroups = 4;             // projection waves along the vocabulary ...
+constexpr int kPGroups = 2;             // ... and along the positions
 constexpr int kVB = 2;                  // 32-row vocabulary blocks per wave (A fragments)
 constexpr int kVocabPerWave = 32 * kVB; // 64 vocabulary rows per wave
-constexpr int kVocabTile = kWaves * kVocabPerWave;   // 256 vocabulary rows per tile
+constexpr int kVocabTile = kVGroups * kVocabPerWave;   // 256 vocabulary rows per tile
 constexpr int kKChunk = 64;             // hidden elements per LDS stage
 constexpr int kMaxGroups = 256;         // vocabulary groups (partials per position)
 
@@ -51,6 +54,8 @@ typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 
 constexpr double kLn2 = 0.693147180559945309417232121458176568;
+constexpr float kMasked = -2.0e30f;      // logit (bits) of vocabulary ids past V
+constexpr double kMinTemperature = 1e-4;  // keeps tempered fp32 logits finite
 constexpr double kLog2e = 1.442695040888963407359924681001892137;
 
 struct ProjArgs {
@@ -151,44 +156,48 @@ constexpr int kNonTemporal = 2;   // streaming (nt) cache policy for W
 // ---------------------------------------------------------------------------
 // k_project: fused projection + tempered softmax-entropy / argmax / Gumbel-max
 // ---------------------------------------------------------------------------
-// Workgroup = 4 waves, one per SIMD; tile = 256 vocabulary rows (64 per wave,
-// two 32-row blocks) x MROWS = 32*MB positions.  MFMA
-// v_mfma_f32_32x32x16_bf16 with A = W (vocabulary along the MFMA rows) and
-// B = H (positions along the MFMA columns): every H fragment read from LDS
-// feeds two MFMAs, and lane l of a wave holds, per 32-position block and per
-// vocabulary block, 16 logits of ONE position (column l%32) at vocabulary
-// rows 8q + 4(l/32) + e (q, e = 0..3): groups of four consecutive ids, i.e.
-// exactly the four words of one Philox call.
+// Workgroup = 8 waves, two per SIMD (one wave per SIMD cannot stream 128-bit
+// LDS reads at the rate the MFMAs consume them).  Tile = 256 vocabulary rows x
+// MROWS = 32*MB positions; wave w covers vocabulary rows 64*(w%4) .. +63 (two
+// 32-row blocks) and positions (w/4)*MROWS/2 .. +MROWS/2-1.
 //
-// K loop: per 64-element hidden chunk each lane loads, for its two vocabulary
-// rows, the 64 contiguous bytes W[v][32h .. 32h+31] (h = lane/32), kWDepth
-// chunks deep in registers; the workgroup stages the [MROWS x 64] H chunk in
-// LDS (double buffered, 16-byte segments XOR-swizzled by row).  MFMA
-// sub-step s (0..3) uses hidden elements 32h + 8s .. +7 for lane half h in
-// both operands: the same permutation of k on A and B, so the products summed
-// are exactly those of the plain dot product.
+// MFMA v_mfma_f32_32x32x16_bf16 with A = W (vocabulary along the MFMA rows)
+// and B = H (positions along the MFMA columns): lane l holds, per 32-position
+// block and vocabulary block, 16 logits of ONE position (column l%32) at
+// vocabulary rows 8q + 4(l/32) + e (q, e = 0..3), i.e. groups of four
+// consecutive ids: exactly the four words of one Philox call.
+//
+// K loop, per 64-element hidden chunk: the workgroup reads the W chunk
+// [256 x 64] eight lanes per 128-byte line (two chunks in flight, in
+// registers) and the H chunk [MROWS x 64] (L2-resident, one chunk ahead), and
+// stages both in double-buffered, swizzled LDS, from which the MFMA fragments
+// are read.  MFMA sub-step s (0..3) uses hidden elements 32h + 8s .. +7 for
+// lane half h in both operands: the same permutation of k on A and B, so the
+// products summed are exactly those of the plain dot product.
 //
 // kUniformKey: every 32-row block lies inside one canvas (L % 32 == 0), so the
 // Philox key is wave-uniform and lives in scalar registers.
 template <int MB, bool kLogits, bool kUniformKey>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_project(const ProjArgs a) {
+  static_assert(MB == 2 || MB == 4 || MB == 8, "MB");
   constexpr int MROWS = 32 * MB;
-  constexpr int HSEG = MROWS * (kKChunk / 8) / kThreads;   // 16-byte H segments per thread
-  static_assert(HSEG >= 1, "tile too small");
-  static_assert(MB == 1 || MB == 2 || MB == 4 || MB == 8, "MB");
-  // LDS: H chunk [MROWS x 64] and W chunk [256 x 64] bf16, double buffered,
-  // 16-byte segments XOR-swizzled by row; then the running records.
+  constexpr int MBW = MB / kPGroups;                      // position blocks per wave
+  constexpr int PPW = MROWS / kPGroups;                   // positions per wave
+  constexpr int HSEG = MROWS * (kKChunk / 8) / kPThreads; // 16-byte H segments per thread
+  constexpr int WSEG = kVocabTile * (kKChunk / 8) / kPThreads;  // 16-byte W segments per thread
   constexpr int HBUF = MROWS * kKChunk * 2;
   constexpr int WBUF = kVocabTile * kKChunk * 2;
+  static_assert(HSEG >= 1 && WSEG == 4, "tiling");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * HBUF + 2 * WBUF];
-  // running record of every (wave, position) over the tiles seen so far
-  __shared__ __attribute__((aligned(16))) Rec recs[kWaves * MROWS];
+  // running record of every (wave, position of its group) over the tiles seen
+  __shared__ __attribute__((aligned(16))) Rec recs[8 * PPW];
   uint8_t* const hbuf0 = smem;
   uint8_t* const wbuf0 = smem + 2 * HBUF;
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
+  const int wv = wave & (kVGroups - 1), wp = wave / kVGroups;
 
   if (blockIdx.x == 0 && tid < a.B) a.counters[tid] = 0;
 
@@ -202,17 +211,17 @@ k_project(const ProjArgs a) {
     if (all_done) return;
   }
 
-  for (int i = tid; i < kWaves * MROWS; i += kThreads) rec_store(recs + i, rec_empty());
+  for (int i = tid; i < 8 * PPW; i += kPThreads) rec_store(recs + i, rec_empty());
   // (the first __syncthreads of the tile loop orders these writes)
 
   const int nk = (a.d + kKChunk - 1) / kKChunk;
   const size_t d = (size_t)a.d;
 
   for (int vt = g; vt < a.n_vtiles; vt += a.P) {
-    const int vbase = vt * kVocabTile + wave * kVocabPerWave;
+    const int vbase = vt * kVocabTile + wv * kVocabPerWave;
     // Buffer resources for this tile: rows past the end of W (or of the
     // M tile) lie beyond num_records and read as zero without a memory
-    // access; so does any offset set to kOOB.  All offsets are in the
+    // access; so does any offset with bit 31 set.  All offsets are in the
     // 32-bit VGPR offset so the range check covers them.
     const int vrows = min(kVocabTile, a.V - vt * kVocabTile);
     const __amdgpu_buffer_rsrc_t wres = __builtin_amdgcn_make_buffer_rsrc(
@@ -220,31 +229,31 @@ k_project(const ProjArgs a) {
     const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.H + (size_t)row0 * d), (short)0, (int)((size_t)min(MROWS, a.M - row0) * d * 2),
         kRsrcWord3);
-    // W rows of this wave are loaded fully coalesced: instruction j covers
-    // rows 8j .. 8j+7 of the wave's 64, lane l reading 16 bytes at segment
-    // l%8 of row l/8 (eight lanes per 128-byte line).
-    const uint32_t woff = (uint32_t)((wave * kVocabPerWave + (lane >> 3)) * d * 2 + (lane & 7) * 16);
-    const uint32_t wstride = (uint32_t)(8 * d * 2);    // 8 rows
+    // Wave w loads tile rows 32w .. 32w+31 of W, instruction j covering rows
+    // 32w + 8j .. +7 with lane l reading 16 bytes at segment l%8 of row l/8
+    // (eight lanes per 128-byte line).
+    const uint32_t woff = (uint32_t)((32 * wave + (lane >> 3)) * d * 2 + (lane & 7) * 16);
+    const uint32_t wstride = (uint32_t)(8 * d * 2);                     // 8 rows
     const uint32_t hoff = (uint32_t)((tid >> 3) * d * 2 + (tid & 7) * 16);
-    const uint32_t hstride = (uint32_t)(32 * d * 2);   // 32 rows
+    const uint32_t hstride = (uint32_t)((kPThreads / 8) * d * 2);      // 64 rows
 
     // Loads of hidden elements past d (including whole chunks past the end)
     // get bit 31 set in their offset: beyond num_records, they read zeros
     // without a memory access.  Built with bit operations, not a select, so
     // the loop body stays straight-line code.
-    auto load_w = [&](int c, u32x4_t (&dst)[8]) {
+    auto load_w = [&](int c, u32x4_t (&dst)[WSEG]) {
       const uint32_t oob = (uint32_t)(c * kKChunk + (lane & 7) * 8 >= a.d) << 31;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
+      for (int j = 0; j < WSEG; ++j) {
         const uint32_t off = (woff + (uint32_t)j * wstride + (uint32_t)(c * kKChunk * 2)) | oob;
         dst[j] = __builtin_amdgcn_raw_buffer_load_b128(wres, off, 0, kNonTemporal);
       }
     };
-    auto store_w = [&](int buf, const u32x4_t (&src)[8]) {
+    auto store_w = [&](int buf, const u32x4_t (&src)[WSEG]) {
       uint8_t* base = wbuf0 + buf * WBUF;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = wave * kVocabPerWave + 8 * j + (lane >> 3);
+      for (int j = 0; j < WSEG; ++j) {
+        const int r = 32 * wave + 8 * j + (lane >> 3);
         *(u32x4_t*)(base + r * 128 + (((lane & 7) ^ swz(r)) << 4)) = src[j];
       }
     };
@@ -260,17 +269,17 @@ k_project(const ProjArgs a) {
       uint8_t* base = hbuf0 + buf * HBUF;
 #pragma unroll
       for (int i = 0; i < HSEG; ++i) {
-        const int idx = i * kThreads + tid;
+        const int idx = i * kPThreads + tid;
         const int r = idx >> 3, e = idx & 7;
         *(u32x4_t*)(base + r * 128 + ((e ^ swz(r)) << 4)) = src[i];
       }
     };
 
-    f32x16_t acc[kVB][MB];
+    f32x16_t acc[kVB][MBW];
 #pragma unroll
     for (int vb = 0; vb < kVB; ++vb)
 #pragma unroll
-      for (int pb = 0; pb < MB; ++pb)
+      for (int pb = 0; pb < MBW; ++pb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[vb][pb][i] = 0.f;
 
@@ -281,7 +290,8 @@ k_project(const ProjArgs a) {
     // wait for H at the end of the chunk leaves the W prefetch in flight.
     // Chunks past the end read zeros and add exact zeros, so the loop runs
     // whole pairs of chunks and the register ring index stays static.
-    auto chunk = [&](int c, u32x4_t (&wload)[8], const u32x4_t (&wstore)[8], u32x4_t (&hs)[HSEG]) {
+    auto chunk = [&](int c, u32x4_t (&wload)[WSEG], const u32x4_t (&wstore)[WSEG],
+                     u32x4_t (&hs)[HSEG]) {
       __builtin_amdgcn_sched_barrier(0);
       load_h(c + 1, hs);
       __builtin_amdgcn_sched_barrier(0);
@@ -289,27 +299,33 @@ k_project(const ProjArgs a) {
       __builtin_amdgcn_sched_barrier(0);
       const uint8_t* hb = hbuf0 + (c & 1) * HBUF;
       const uint8_t* wb = wbuf0 + (c & 1) * WBUF;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      // Fragments of one sub-step are read from LDS, then its MFMAs issue
+      // (the other wave on the SIMD covers the read latency).
+      auto load_frags = [&](int s, bf16x8_t (&av)[kVB], bf16x8_t (&bv)[MBW]) {
         const int e = (4 * half + s) ^ swz(col);
-        bf16x8_t av[kVB];
 #pragma unroll
         for (int vb = 0; vb < kVB; ++vb)
-          av[vb] = as_bf16x8(*(const u32x4_t*)(wb + (wave * kVocabPerWave + vb * 32 + col) * 128 + (e << 4)));
+          av[vb] = as_bf16x8(*(const u32x4_t*)(wb + (wv * kVocabPerWave + vb * 32 + col) * 128 + (e << 4)));
 #pragma unroll
-        for (int pb = 0; pb < MB; ++pb) {
-          const bf16x8_t bv = as_bf16x8(*(const u32x4_t*)(hb + (pb * 32 + col) * 128 + (e << 4)));
+        for (int pb = 0; pb < MBW; ++pb)
+          bv[pb] = as_bf16x8(*(const u32x4_t*)(hb + (wp * PPW + pb * 32 + col) * 128 + (e << 4)));
+      };
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t af[kVB], bf[MBW];
+        load_frags(s, af, bf);
+#pragma unroll
+        for (int pb = 0; pb < MBW; ++pb)
 #pragma unroll
           for (int vb = 0; vb < kVB; ++vb)
-            acc[vb][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[vb], bv, acc[vb][pb], 0, 0, 0);
-        }
+            acc[vb][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[vb], bf[pb], acc[vb][pb], 0, 0, 0);
       }
       store_h((c + 1) & 1, hs);
       store_w((c + 1) & 1, wstore);
       __syncthreads();
     };
 
-    u32x4_t wx[8], wy[8], hs[HSEG];
+    u32x4_t wx[WSEG], wy[WSEG], hs[HSEG];
     __syncthreads();   // previous tile's readers of smem are done
     load_w(0, wx);
     load_w(1, wy);
@@ -326,31 +342,24 @@ k_project(const ProjArgs a) {
     // One loop body for all blocks (not unrolled: it is long); the switch
     // keeps every accumulator index static so the tile stays in registers.
 #pragma unroll 1
-    for (int pb = 0; pb < MB; ++pb) {
+    for (int pb = 0; pb < MBW; ++pb) {
       f32x16_t z[kVB];
       switch (pb) {
 #define DGD_TAKE(P)                                            \
   case P:                                                      \
     _Pragma("unroll") for (int vb = 0; vb < kVB; ++vb)         \
-        z[vb] = acc[vb][(P) < MB ? (P) : 0];                   \
+        z[vb] = acc[vb][(P) < MBW ? (P) : 0];                  \
     break;
         DGD_TAKE(0) DGD_TAKE(1) DGD_TAKE(2) DGD_TAKE(3)
-        DGD_TAKE(4) DGD_TAKE(5) DGD_TAKE(6) DGD_TAKE(7)
 #undef DGD_TAKE
       }
-      const int r = row0 + pb * 32 + col;
+      const int r = row0 + wp * PPW + pb * 32 + col;
       const bool rvalid = r < a.M;
       int cv = rvalid ? r / a.L : 0;
       if constexpr (kUniformKey) cv = __builtin_amdgcn_readfirstlane(cv);
       const int p = r - cv * a.L;
       const uint32_t pabs = (uint32_t)(a.block * a.L + p);
       const uint32_t key0 = a.key[cv][0], key1 = a.key[cv][1];
-
-      float x[kVB * 16];
-#pragma unroll
-      for (int vb = 0; vb < kVB; ++vb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) x[vb * 16 + i] = z[vb][i] * a.c2;
 
       if constexpr (kLogits) {
         if (rvalid) {
@@ -367,14 +376,19 @@ k_project(const ProjArgs a) {
         }
       }
 
+      // Tempered logits in bits: x = z * c2, recomputed in each pass rather
+      // than kept (registers are the scarce resource here).  The multiply is
+      // never fused with the following add, so every pass sees the same x.
       // value index i = vb*16 + 4q + e  <->  vocabulary id vbase + vb*32 + 8q + 4h + e.
-      // In a ragged last tile, ids past V get the sentinel logit kNeg: they
-      // add exact zeros to S and A and never win the argmax or the sample.
+      // In a ragged last tile, ids past V get the logit kMasked, far below
+      // the running-max start kNeg: they add exact zeros to S and A and never
+      // win the argmax or the sample.
+      const float c2 = a.c2;
       if (vbase + kVocabPerWave > a.V) {
 #pragma unroll
         for (int i = 0; i < kVB * 16; ++i) {
           const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
-          x[i] = v < a.V ? x[i] : kNeg;
+          z[i >> 4][i & 15] = v < a.V ? z[i >> 4][i & 15] : kMasked / c2;
         }
       }
       float m = kNeg;
@@ -382,16 +396,22 @@ k_project(const ProjArgs a) {
 #pragma unroll
       for (int i = 0; i < kVB * 16; ++i) {   // first maximum (ids increase with i)
         const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
-        am = x[i] > m ? v : am;
-        m = fmaxf(m, x[i]);
+        const float x = __fmul_rn(z[i >> 4][i & 15], c2);
+        am = x > m ? v : am;
+        m = fmaxf(m, x);
       }
+      // Scheduling barriers bound how far the scheduler may hoist work across
+      // the value loops: unbounded, it keeps every intermediate of the block
+      // live at once and spills.
+      __builtin_amdgcn_sched_barrier(0);
       float S = 0.f, A = 0.f;
 #pragma unroll
       for (int i = 0; i < kVB * 16; ++i) {
-        const float dx = x[i] - m;
+        const float dx = __fmul_rn(z[i >> 4][i & 15], c2) - m;
         const float e = fexp2(dx);
         S += e;
         A = fmaf(dx, e, A);
+        if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
       }
       float y1 = kNeg, y2 = kNeg;
       int i1 = kNoIndex;
@@ -402,11 +422,13 @@ k_project(const ProjArgs a) {
         const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {   // top two, first index on ties
-          const float y = x[4 * grp + e] + gumbel_bits(words[e]);
+          const int i = 4 * grp + e;
+          const float y = __fmul_rn(z[i >> 4][i & 15], c2) + gumbel_bits(words[e]);
           y2 = fmaxf(y2, fminf(y, y1));
           i1 = y > y1 ? v0 + e : i1;
           y1 = fmaxf(y1, y);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
       Rec loc;
       loc.m = m; loc.S = S; loc.A = A; loc.am = am;
@@ -414,18 +436,19 @@ k_project(const ProjArgs a) {
       const Rec oth = rec_shfl_xor(loc, 32);
       const Rec wrec = rec_merge(rec_pick(half == 0, loc, oth), rec_pick(half == 0, oth, loc));
       if (half == 0) {
-        Rec* slot = recs + wave * MROWS + pb * 32 + col;
+        Rec* slot = recs + wave * PPW + pb * 32 + col;
         rec_store(slot, rec_merge(rec_load(slot), wrec));
       }
     }
   }
 
-  // ---------------- merge the four waves (fixed order) and write ----------
+  // ------- merge the four vocabulary waves of each position (fixed order) -------
   __syncthreads();
-  for (int t = tid; t < MROWS; t += kThreads) {
-    Rec r = rec_load(recs + t);
+  for (int t = tid; t < MROWS; t += kPThreads) {
+    const int gp = t / PPW, lp = t % PPW;
+    Rec r = rec_load(recs + (gp * kVGroups) * PPW + lp);
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = rec_merge(r, rec_load(recs + w * MROWS + t));
+    for (int w = 1; w < kVGroups; ++w) r = rec_merge(r, rec_load(recs + (gp * kVGroups + w) * PPW + lp));
     const int row = row0 + t;
     if (row < a.M) rec_store(a.part + (size_t)row * a.P + g, r);
   }
@@ -746,9 +769,9 @@ int check_params(const dgd_params* prm) {
   if (!finite01(prm->t_min) || !finite01(prm->t_max))
     return fail(DGD_EINVAL, "t_min=%g / t_max=%g must be finite and in [0, 1]", prm->t_min, prm->t_max);
   const double tlast = (double)prm->t_max + ((double)(N - 1) / N) * ((double)prm->t_min - prm->t_max);
-  if (!(prm->t_max > 0.f) || !(tlast > 0.0))
-    return fail(DGD_EINVAL, "temperature schedule reaches T <= 0 (t_min=%g, t_max=%g)", prm->t_min,
-                prm->t_max);
+  if (!(prm->t_max >= kMinTemperature) || !(tlast >= kMinTemperature))
+    return fail(DGD_EINVAL, "temperature schedule goes below %g (t_min=%g, t_max=%g)",
+                kMinTemperature, prm->t_min, prm->t_max);
   if (!finite01(prm->confidence)) return fail(DGD_EINVAL, "confidence=%g outside [0, 1]", prm->confidence);
   if (prm->stability_threshold < 0 || prm->stability_threshold > DGD_MAX_STEPS)
     return fail(DGD_EINVAL, "stability_threshold=%d outside [0, 1024]", prm->stability_threshold);
@@ -841,11 +864,11 @@ struct Timer {
 template <int MB>
 void launch_project_mb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits, bool uniform) {
   if (logits) {
-    if (uniform) hipLaunchKernelGGL((k_project<MB, true, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_project<MB, true, false>), grid, dim3(kThreads), 0, s, a);
+    if (uniform) hipLaunchKernelGGL((k_project<MB, true, true>), grid, dim3(kPThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_project<MB, true, false>), grid, dim3(kPThreads), 0, s, a);
   } else {
-    if (uniform) hipLaunchKernelGGL((k_project<MB, false, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_project<MB, false, false>), grid, dim3(kThreads), 0, s, a);
+    if (uniform) hipLaunchKernelGGL((k_project<MB, false, true>), grid, dim3(kPThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_project<MB, false, false>), grid, dim3(kPThreads), 0, s, a);
   }
 }
 
@@ -874,7 +897,7 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   pa.block = block; pa.gstep = gstep;
   pa.c2 = (float)(kLog2e / T);
   fill_keys(pa.key, seed, B);
-  const int MB = M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8;
+  const int MB = M <= 64 ? 2 : M <= 128 ? 4 : 8;
   pa.n_mtiles = (M + 32 * MB - 1) / (32 * MB);
   const dim3 grid1(pa.n_mtiles * pa.P);
   int rc = timer.begin(stream);
@@ -882,7 +905,6 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   const bool lg = ctx->logits != nullptr;
   const bool uni = (L % 32) == 0;
   switch (MB) {
-    case 1: launch_project_mb<1>(pa, grid1, stream, lg, uni); break;
     case 2: launch_project_mb<2>(pa, grid1, stream, lg, uni); break;
     case 4: launch_project_mb<4>(pa, grid1, stream, lg, uni); break;
     default: launch_project_mb<8>(pa, grid1, stream, lg, uni); break;
