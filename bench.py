@@ -73,6 +73,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed loop (for rocprofv3 runs)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="before the timed loop, run one device-to-device copy of this many MiB "
+                         "(a known-size kernel against which HBM byte counters are scaled)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the denoising step of "
@@ -108,6 +111,16 @@ def main():
             if s == 0:
                 dgd.dgd_init_block(canvas, committed, b, params, wl.seeds, ctx)
             dgd.dgd_step(Hd[b, s].reshape(-1), Wd, canvas, committed, b, s, params, wl.seeds, ctx)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
+        del src, dst
 
     log(f"[bench] warmup {args.warmup} steps")
     run_steps(args.warmup)
