@@ -70,6 +70,8 @@ def main():
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", default="gemma_vocab")
+    ap.add_argument("--layout", choices=["packed", "rows"], default="packed",
+                    help="vocabulary table layout: packed once before timing (default) or row-major")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed loop (for rocprofv3 runs)")
@@ -93,8 +95,14 @@ def main():
     W, Hs = make_workload_arrays(wl, threads=16)
     log(f"[bench] generated {wl.name} inputs in {time.perf_counter() - t0:.1f}s")
     Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+    layout = dgd.DGD_VOCAB_PACKED if args.layout == "packed" else dgd.DGD_VOCAB_ROWS
+    if layout == dgd.DGD_VOCAB_PACKED:
+        # one-time rewrite of the table into the projection's streaming order
+        Wd = dgd.pack_vocab(Wd, wl.V, wl.d)
+        torch.cuda.synchronize()
     Hd = torch.from_numpy(Hs.view(np.int16)).to(dev)
-    ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev, outputs=False)
+    ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev, outputs=False,
+                      vocab_layout=layout)
     params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence, wl.stability_threshold,
                              wl.freeze, wl.final_emit)
     canvas = torch.zeros(wl.B * wl.G, dtype=torch.int32, device=dev)
@@ -157,7 +165,8 @@ def main():
              "frac": hbm_frac} if bound == "hbm" else
             {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": mfma_frac})
-    roof.update({"traffic": None, "kernel": "k_project", "kernel_avg_us": k1_avg_s * 1e6,
+    roof.update({"traffic": None,
+                 "kernel": "k_project_packed" if layout == dgd.DGD_VOCAB_PACKED else "k_project", "kernel_avg_us": k1_avg_s * 1e6,
                  "kernel_launches": k1_n, "algorithmic_bytes_per_launch": alg_bytes,
                  "flops_per_launch": flops,
                  "other": {"hbm_GBs": gbs, "hbm_frac": hbm_frac, "mfma_TFLOPs": tflops,
@@ -178,7 +187,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "canvases": wl.B, "canvas_len": wl.L, "vocab": wl.V,
-                   "hidden": wl.d, "gen_length": wl.G, "num_inference_steps": wl.N},
+                   "hidden": wl.d, "gen_length": wl.G, "num_inference_steps": wl.N,
+                   "vocab_layout": args.layout},
         "logit_elems_per_s": steps_per_s * M * wl.V,
         "step_frac_of_hbm_floor": (steps_per_s * alg_bytes) / (HBM_PEAK_GBS * 1e9),
         "roofline": roof,

@@ -78,6 +78,10 @@ extern "C" {
 
 typedef uint16_t dgd_bf16;
 
+/* Layouts of the vocabulary table W_vocab accepted by dgd_step / dgd_run. */
+#define DGD_VOCAB_ROWS   0  /* [V][d] row-major: the tied embedding table as is          */
+#define DGD_VOCAB_PACKED 1  /* the output of dgd_pack_vocab() (MFMA fragment order)      */
+
 /* Sampler knobs (node page "Inputs"; TensorSharp doc "3. Sampler contract").
  * Ranges are checked on every call:
  *   num_inference_steps  N in [1, 1024]
@@ -120,6 +124,10 @@ typedef struct dgd_params {
  *   logits      float[B*L*V] z (fp32 accumulator, before temperature); validation only
  *   commit_step int16[B*G]   step index s at which the position was last committed
  *                            (untouched elsewhere; callers pre-fill, e.g. with -1)
+ *   vocab_layout   DGD_VOCAB_ROWS (0) when W_vocab is the [V][d] table itself,
+ *                  DGD_VOCAB_PACKED (1) when it is the output of dgd_pack_vocab()
+ *                  for the same V and d (the faster path: every load of the
+ *                  projection is a contiguous 1 KB MFMA fragment)
  * Optional host outputs (timing): when k1_ms is not NULL the call records HIP
  * events around every launch of the fused projection kernel, synchronises
  * before returning, and writes the summed kernel time in ms to *k1_ms and the
@@ -139,6 +147,7 @@ typedef struct dgd_ctx {
   int16_t* commit_step;
   double*  k1_ms;
   int32_t* k1_launches;
+  int32_t  vocab_layout;   /* DGD_VOCAB_ROWS or DGD_VOCAB_PACKED: how W_vocab is laid out */
 } dgd_ctx;
 
 /* State layout (device, int32/float words, in this order):
@@ -169,8 +178,10 @@ int dgd_init_block(int32_t* canvas, uint8_t* committed, int32_t block,
 
 /* One denoising step (block `block`, step `step` in [0, N)) of every canvas
  * that is not done.  H: device bf16[B*L*d], the final hidden states of the B
- * canvases for this step (row r = c*L + p).  W_vocab: device bf16[V*d], the
- * tied embedding table.  canvas/committed: device int32/uint8[B*G], updated
+ * canvases for this step (row r = c*L + p).  W_vocab: device, the tied
+ * embedding table in the layout ctx->vocab_layout names (bf16[V*d] row-major,
+ * or dgd_packed_vocab_bytes(V, d) bytes from dgd_pack_vocab).  H and W_vocab
+ * must be 16-byte aligned.  canvas/committed: device int32/uint8[B*G], updated
  * in place.  seed: host uint64[B].  The [B*L x V] logits never reach HBM
  * unless ctx->logits asks for them. */
 int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_t* committed,
@@ -185,6 +196,23 @@ int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_
 int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas,
             uint8_t* committed, const dgd_params* params, const uint64_t* seed,
             const dgd_ctx* ctx);
+
+/* Size in bytes of the packed vocabulary table for (V, d):
+ * ceil(V/64)*64 * ceil(d/64)*64 * 2; 0 if V or d is outside the limits. */
+size_t dgd_packed_vocab_bytes(int32_t V, int32_t d);
+
+/* Rewrite the tied embedding table once into the order in which the fused
+ * projection streams it (a permutation of W_vocab's elements, zero-padded to
+ * whole 64-row groups and 64-element hidden chunks).  The table's values are
+ * the ones the pages' unembedding uses (walkthrough, "Setup + Load Model":
+ * tied [V x d] embedding); only the byte order changes.
+ *   W_vocab   device bf16[V*d] row-major, read only
+ *   W_packed  device, dgd_packed_vocab_bytes(V, d) bytes, written; must not
+ *             overlap W_vocab
+ * Both 16-byte aligned.  Enqueued on `stream` (hipStream_t).  Pack once per
+ * table; a packed table serves every later step with ctx->vocab_layout =
+ * DGD_VOCAB_PACKED. */
+int dgd_pack_vocab(const dgd_bf16* W_vocab, dgd_bf16* W_packed, int32_t V, int32_t d, void* stream);
 
 /* Validation helper: for n 32-bit Philox words (device uint32[n]) write the
  * Gumbel noise the fused step adds to its logits, in base-2 units:

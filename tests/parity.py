@@ -183,15 +183,17 @@ def compare_step(rep: Report, tag: str, before: O.CanvasState, after: O.CanvasSt
 class Lockstep:
     """Drive the HIP library and the oracle side by side on one workload."""
 
-    def __init__(self, wl, W, Hs, device, logits=False):
+    def __init__(self, wl, W, Hs, device, logits=False, layout=0):
         import torch
         from uniform_state_discrete_step_amd import dgd
         self.dgd, self.torch = dgd, torch
         self.wl, self.W, self.Hs, self.dev = wl, W, Hs, device
         self.Wd = torch.from_numpy(W.view(np.int16)).to(device)
+        if layout == dgd.DGD_VOCAB_PACKED:
+            self.Wd = dgd.pack_vocab(self.Wd, wl.V, wl.d)
         self.Hd = torch.from_numpy(Hs.view(np.int16)).to(device)
         self.ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=device,
-                               logits=logits)
+                               logits=logits, vocab_layout=layout)
         self.params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence,
                                       wl.stability_threshold, wl.freeze, wl.final_emit)
         self.P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,

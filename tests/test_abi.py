@@ -58,6 +58,7 @@ def _ctx(**kw):
     c.workspace = kw.get("workspace", FAKE * 16)
     c.workspace_bytes = kw.get("workspace_bytes", 1 << 30)
     c.state = kw.get("state", FAKE)
+    c.vocab_layout = kw.get("vocab_layout", 0)
     return c
 
 
@@ -103,6 +104,8 @@ def test_invalid_knobs_are_refused(lib, kw, code):
     (dict(workspace=None), dgd.DGD_EINVAL),
     (dict(workspace=FAKE * 16 + 8), dgd.DGD_EINVAL),
     (dict(workspace_bytes=100), dgd.DGD_EWORKSPACE),
+    (dict(vocab_layout=2), dgd.DGD_EINVAL),
+    (dict(vocab_layout=-1), dgd.DGD_EINVAL),
 ])
 def test_invalid_shapes_and_buffers_are_refused(lib, kw, code):
     assert _step(lib, _ctx(**kw)) == code
@@ -114,6 +117,8 @@ def test_invalid_step_block_and_pointers_are_refused(lib):
     assert _step(lib, _ctx(), block=1) == dgd.DGD_EINVAL
     assert _step(lib, _ctx(), H=None) == dgd.DGD_EINVAL
     assert _step(lib, _ctx(), W=None) == dgd.DGD_EINVAL
+    assert _step(lib, _ctx(), H=FAKE + 8) == dgd.DGD_EINVAL          # not 16-byte aligned
+    assert _step(lib, _ctx(vocab_layout=1), W=FAKE + 2) == dgd.DGD_EINVAL
     p = dgd.make_params(N=8)
     assert lib.dgd_step(FAKE, FAKE, FAKE, FAKE, 0, 0, ctypes.byref(p), None, ctypes.byref(_ctx())) == dgd.DGD_EINVAL
     assert lib.dgd_step(FAKE, FAKE, FAKE, FAKE, 0, 0, None, None, ctypes.byref(_ctx())) == dgd.DGD_EINVAL
@@ -133,3 +138,20 @@ def test_binding_refuses_missing_library(tmp_path):
             dgd.load_library(str(tmp_path / "missing.so"))
         finally:
             dgd._lib = saved
+
+
+def test_packed_vocab_size_and_refusals(lib):
+    # whole 64-row groups and 64-element hidden chunks, 2 bytes each
+    assert dgd.dgd_packed_vocab_bytes(262144, 2816) == 262144 * 2816 * 2
+    assert dgd.dgd_packed_vocab_bytes(1001, 72) == 1024 * 128 * 2
+    assert dgd.dgd_packed_vocab_bytes(1, 8) == 64 * 64 * 2
+    for bad in [(0, 64), (1024, 0), (1024, 60), ((1 << 24) + 1, 64), (1024, 65536 + 8)]:
+        assert dgd.dgd_packed_vocab_bytes(*bad) == 0, bad
+    assert lib.dgd_pack_vocab(None, FAKE, 64, 64, None) == dgd.DGD_EINVAL
+    assert lib.dgd_pack_vocab(FAKE, None, 64, 64, None) == dgd.DGD_EINVAL
+    assert lib.dgd_pack_vocab(FAKE, FAKE * 4, 0, 64, None) == dgd.DGD_EUNSUPPORTED
+    assert lib.dgd_pack_vocab(FAKE, FAKE * 4, 64, 12, None) == dgd.DGD_EUNSUPPORTED
+    assert lib.dgd_pack_vocab(FAKE + 4, FAKE * 4, 64, 64, None) == dgd.DGD_EINVAL
+    # destination overlapping the source
+    assert lib.dgd_pack_vocab(FAKE, FAKE + 64 * 64, 64, 64, None) == dgd.DGD_EINVAL
+    assert dgd.dgd_last_error()

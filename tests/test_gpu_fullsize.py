@@ -1,5 +1,6 @@
 """GPU parity at the full workload sizes (V = 262144, d = 2816), in the launch
-configuration the benchmark times.
+configuration the benchmark times (packed vocabulary table), and on the
+row-major table.
 
 The oracle cannot recompute every position of every step at these sizes, so
 the checks are split:
@@ -34,16 +35,21 @@ def dev():
 class FullRun:
     """Step a workload on the GPU with dgd_step and check every step."""
 
-    def __init__(self, wl, dev, W=None, Hs=None):
+    def __init__(self, wl, dev, W=None, Hs=None, layout=1, Wd=None):
         import torch
         from uniform_state_discrete_step_amd import dgd
         self.torch, self.dgd, self.wl, self.dev = torch, dgd, wl, dev
         if W is None:
             W, Hs = make_workload_arrays(wl, threads=16)
         self.W, self.Hs = W, Hs
-        self.Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+        if Wd is None:
+            Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+            if layout == dgd.DGD_VOCAB_PACKED:
+                Wd = dgd.pack_vocab(Wd, wl.V, wl.d)
+        self.Wd = Wd
         self.Hd = torch.from_numpy(Hs.view(np.int16)).to(dev)
-        self.ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev)
+        self.ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev,
+                               vocab_layout=layout)
         self.params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence,
                                       wl.stability_threshold, wl.freeze, wl.final_emit)
         self.P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,
@@ -127,9 +133,11 @@ def _check(rep, name):
     assert not rep.failures, "\n".join(rep.failures)
 
 
-def test_gemma_vocab_full_run(dev):
+@pytest.mark.parametrize("layout", [1, 0], ids=["packed", "rows"])
+def test_gemma_vocab_full_run(dev, layout):
     wl = WORKLOADS["gemma_vocab"]
-    _check(FullRun(wl, dev).run(sample_every=6, rows_per_canvas=6), wl.name)
+    _check(FullRun(wl, dev, layout=layout).run(sample_every=6, rows_per_canvas=6),
+           f"{wl.name} layout={layout}")
 
 
 def test_batched_full_run_and_batch_invariance(dev):
@@ -141,8 +149,8 @@ def test_batched_full_run_and_batch_invariance(dev):
     c = 5
     alone = shrink(wl, name="batched_c5", B=1, seeds=(wl.seeds[c],), bounds=(wl.bounds[c],))
     Hs1 = np.ascontiguousarray(run.Hs[:, :, c:c + 1])
-    solo = FullRun(alone, dev, W=run.W, Hs=Hs1)
-    solo.Wd, solo.W64 = run.Wd, run.W64
+    solo = FullRun(alone, dev, W=run.W, Hs=Hs1, Wd=run.Wd)
+    solo.W64 = run.W64
     _check(solo.run(sample_every=1000, rows_per_canvas=1), alone.name)
     torch.cuda.synchronize()
     assert np.array_equal(solo.canvas.cpu().numpy(),
@@ -151,9 +159,11 @@ def test_batched_full_run_and_batch_invariance(dev):
                           run.committed[c * wl.G:(c + 1) * wl.G].cpu().numpy())
 
 
-def test_multi_block_full_run(dev):
+@pytest.mark.parametrize("layout", [1, 0], ids=["packed", "rows"])
+def test_multi_block_full_run(dev, layout):
     wl = WORKLOADS["multi_block"]
-    _check(FullRun(wl, dev).run(sample_every=16, rows_per_canvas=3), wl.name)
+    _check(FullRun(wl, dev, layout=layout).run(sample_every=16, rows_per_canvas=3),
+           f"{wl.name} layout={layout}")
 
 
 def test_dgd_run_matches_stepping_and_is_deterministic(dev):

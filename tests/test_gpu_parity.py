@@ -25,16 +25,23 @@ def dev():
     return torch.device("cuda:0")
 
 
+# every lockstep case runs on both vocabulary layouts: 0 = row-major table,
+# 1 = the packed table of dgd_pack_vocab
+@pytest.fixture(params=[0, 1], ids=["rows", "packed"])
+def layout(request):
+    return request.param
+
+
 def bf16(x):
     return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
 
 
-def run_lockstep(wl, dev, W=None, Hs=None, logits=False, **kw):
+def run_lockstep(wl, dev, W=None, Hs=None, logits=False, layout=0, **kw):
     if W is None:
         W, Hs = make_workload_arrays(wl, threads=8)
-    ls = Lockstep(wl, W, Hs, dev, logits=logits)
+    ls = Lockstep(wl, W, Hs, dev, logits=logits, layout=layout)
     rep = ls.run(**kw)
-    print(f"\n[{wl.name} B={wl.B} L={wl.L} G={wl.G} V={wl.V} d={wl.d} N={wl.N} "
+    print(f"\n[{wl.name} layout={layout} B={wl.B} L={wl.L} G={wl.G} V={wl.V} d={wl.d} N={wl.N} "
           f"freeze={wl.freeze} final_emit={wl.final_emit}] {rep.summary()}", flush=True)
     assert not rep.failures, "\n".join(rep.failures)
     return ls, rep
@@ -59,8 +66,8 @@ def test_gumbel_transform_every_cell(dev):
     assert err.max() <= 2e-5
 
 
-def test_tiny_lockstep(dev):
-    run_lockstep(WORKLOADS["tiny"], dev)
+def test_tiny_lockstep(dev, layout):
+    run_lockstep(WORKLOADS["tiny"], dev, layout=layout)
 
 
 @pytest.mark.parametrize("variant", [
@@ -71,8 +78,8 @@ def test_tiny_lockstep(dev):
     dict(N=1),
     dict(N=3, t_min=0.0, t_max=1.0),
 ])
-def test_tiny_variants(dev, variant):
-    run_lockstep(shrink(WORKLOADS["tiny"], **variant), dev)
+def test_tiny_variants(dev, variant, layout):
+    run_lockstep(shrink(WORKLOADS["tiny"], **variant), dev, layout=layout)
 
 
 @pytest.mark.parametrize("shape", [
@@ -81,21 +88,21 @@ def test_tiny_variants(dev, variant):
     dict(V=1, d=16, L=5, B=1, G=5, N=3),           # one-token vocabulary
     dict(V=4096, d=136, L=70, B=2, G=70, N=6),     # rows straddle 32-row blocks of one tile
 ])
-def test_ragged_shapes(dev, shape):
+def test_ragged_shapes(dev, shape, layout):
     B = shape["B"]
     wl = shrink(WORKLOADS["tiny"], name="ragged", cfg_seed=7, seeds=tuple(range(B)),
                 bounds=tuple((0.1, 0.3, 0.05)[c % 3] for c in range(B)), **shape)
-    run_lockstep(wl, dev)
+    run_lockstep(wl, dev, layout=layout)
 
 
-def test_small_vocab_lockstep(dev):
-    run_lockstep(WORKLOADS["small_vocab"], dev)
+def test_small_vocab_lockstep(dev, layout):
+    run_lockstep(WORKLOADS["small_vocab"], dev, layout=layout)
 
 
 # ----------------------------------------------------------------------------
-def _logit_check(wl, dev, W, Hs, steps):
+def _logit_check(wl, dev, W, Hs, steps, layout):
     import torch
-    ls = Lockstep(wl, W, Hs, dev, logits=True)
+    ls = Lockstep(wl, W, Hs, dev, logits=True, layout=layout)
     ls.run(steps=steps)
     torch.cuda.synchronize()
     z_gpu = ls.ctx.logits.cpu().numpy().reshape(wl.B * wl.L, wl.V).astype(np.float64)
@@ -109,19 +116,19 @@ def _logit_check(wl, dev, W, Hs, steps):
     return z_gpu, z
 
 
-def test_logits_tiny(dev):
+def test_logits_tiny(dev, layout):
     wl = WORKLOADS["tiny"]
     W, Hs = make_workload_arrays(wl, threads=1)
-    _logit_check(wl, dev, W, Hs, steps=[0, 1, 2])
+    _logit_check(wl, dev, W, Hs, steps=[0, 1, 2], layout=layout)
 
 
-def test_logits_small_vocab(dev):
+def test_logits_small_vocab(dev, layout):
     wl = WORKLOADS["small_vocab"]
     W, Hs = make_workload_arrays(wl, threads=8)
-    _logit_check(wl, dev, W, Hs, steps=[0])
+    _logit_check(wl, dev, W, Hs, steps=[0], layout=layout)
 
 
-def test_projection_is_exact_on_small_integers(dev):
+def test_projection_is_exact_on_small_integers(dev, layout):
     """Small-integer bf16 H and W: every fp32 partial sum is exact, so the
     logits must equal the exact integer dot products bit for bit (a wrong
     operand layout, transposition or hidden-chunk mapping cannot pass)."""
@@ -129,24 +136,24 @@ def test_projection_is_exact_on_small_integers(dev):
     rng = np.random.default_rng(11)
     W = bf16(rng.integers(-2, 3, size=(wl.V, wl.d)))
     Hs = bf16(rng.integers(-2, 3, size=(1, wl.N, 1, wl.L, wl.d)))
-    z_gpu, z = _logit_check(wl, dev, W, Hs, steps=[0])
+    z_gpu, z = _logit_check(wl, dev, W, Hs, steps=[0], layout=layout)
     assert np.array_equal(z_gpu, z)
 
 
 # ----------------------------------------------------------------------------
-def test_first_step_from_uniform_logits(dev):
+def test_first_step_from_uniform_logits(dev, layout):
     """H = 0 gives uniform logits: entropy ln V everywhere and one commit, at position 0."""
     wl = shrink(WORKLOADS["tiny"], V=2048, d=64, L=64, G=64, N=4)
     W, _ = make_workload_arrays(wl, threads=1)
     Hs = np.zeros((1, wl.N, 1, wl.L, wl.d), dtype=np.uint16)
-    ls, rep = run_lockstep(wl, dev, W=W, Hs=Hs, steps=[0])
+    ls, rep = run_lockstep(wl, dev, W=W, Hs=Hs, steps=[0], layout=layout)
     H = ls.ctx.entropy.cpu().numpy()
     assert np.all(np.abs(H - math.log(wl.V)) < 1e-5)
     com = ls.committed.cpu().numpy()
     assert com.tolist() == [1] + [0] * (wl.L - 1)
 
 
-def test_convergence_on_stable_peaked_inputs(dev):
+def test_convergence_on_stable_peaked_inputs(dev, layout):
     """Identical one-hot logits every step: the canvas converges at step 1."""
     V = d = 64
     L = 32
@@ -156,7 +163,29 @@ def test_convergence_on_stable_peaked_inputs(dev):
     h = np.zeros((L, d), dtype=np.float32)
     h[np.arange(L), toks] = 60.0
     Hs = np.broadcast_to(bf16(h), (1, wl.N, 1, L, d)).copy()
-    ls, rep = run_lockstep(wl, dev, W=W, Hs=Hs)
+    ls, rep = run_lockstep(wl, dev, W=W, Hs=Hs, layout=layout)
     sv = ls.ctx.state_views()
     assert int(sv["steps_used"][0]) == 2 and int(sv["converged"][0]) == 1
     assert np.array_equal(ls.canvas.cpu().numpy(), toks)
+
+
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("V,d", [(1001, 72), (64, 64), (300, 200), (1, 8)])
+def test_pack_vocab_layout(dev, V, d):
+    """dgd_pack_vocab against the layout include/dgd.h documents, bit for bit:
+    element j of lane l of fragment f, step s, chunk c, row group rg holds
+    W[64 rg + 32 f + l % 32][64 c + 32 (l // 32) + 8 s + j], zeros past V, d."""
+    import torch
+    from uniform_state_discrete_step_amd import dgd
+    rng = np.random.default_rng(V * 1000 + d)
+    W = rng.integers(0, 1 << 16, size=(V, d), dtype=np.uint16)
+    Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+    got = dgd.pack_vocab(Wd, V, d).cpu().numpy().view(np.uint16)
+    n_rg, nk = -(-V // 64), -(-d // 64)
+    Wpad = np.zeros((n_rg * 64, nk * 64), dtype=np.uint16)
+    Wpad[:V, :d] = W
+    rg, c, s, f, l, j = np.meshgrid(np.arange(n_rg), np.arange(nk), np.arange(4), np.arange(2),
+                                    np.arange(64), np.arange(8), indexing="ij")
+    expect = Wpad[64 * rg + 32 * f + l % 32, 64 * c + 32 * (l // 32) + 8 * s + j]
+    assert got.shape[0] == dgd.dgd_packed_vocab_bytes(V, d) // 2 == expect.size
+    assert np.array_equal(got, expect.reshape(-1))

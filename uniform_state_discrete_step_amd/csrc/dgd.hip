@@ -153,6 +153,72 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOOB = 0x80000000u;
 constexpr int kNonTemporal = 2;   // streaming (nt) cache policy for W
 
+// Record of one position over the 64 vocabulary ids held by a lane pair:
+// z[vb][4q + e] (lane half h) is the logit of id vbase + 32 vb + 8 q + 4 h + e.
+// The two halves' records are merged; both lanes return the merged record.
+__device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int half, int V, float c2,
+                                           uint32_t pabs, uint32_t gstep, uint32_t key0,
+                                           uint32_t key1) {
+  // Tempered logits in bits: x = z * c2, recomputed in each pass rather
+  // than kept (registers are the scarce resource here).  The multiply is
+  // never fused with the following add, so every pass sees the same x.
+  // value index i = vb*16 + 4q + e  <->  vocabulary id vbase + vb*32 + 8q + 4h + e.
+  // In a ragged last tile, ids past V get the logit kMasked, far below
+  // the running-max start kNeg: they add exact zeros to S and A and never
+  // win the argmax or the sample.
+  if (vbase + kVocabPerWave > V) {
+#pragma unroll
+    for (int i = 0; i < kVB * 16; ++i) {
+      const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
+      z[i >> 4][i & 15] = v < V ? z[i >> 4][i & 15] : kMasked / c2;
+    }
+  }
+  float m = kNeg;
+  int am = kNoIndex;
+#pragma unroll
+  for (int i = 0; i < kVB * 16; ++i) {   // first maximum (ids increase with i)
+    const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
+    const float x = __fmul_rn(z[i >> 4][i & 15], c2);
+    am = x > m ? v : am;
+    m = fmaxf(m, x);
+  }
+  // Scheduling barriers bound how far the scheduler may hoist work across
+  // the value loops: unbounded, it keeps every intermediate of the block
+  // live at once and spills.
+  __builtin_amdgcn_sched_barrier(0);
+  float S = 0.f, A = 0.f;
+#pragma unroll
+  for (int i = 0; i < kVB * 16; ++i) {
+    const float dx = __fmul_rn(z[i >> 4][i & 15], c2) - m;
+    const float e = fexp2(dx);
+    S += e;
+    A = fmaf(dx, e, A);
+    if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+  }
+  float y1 = kNeg, y2 = kNeg;
+  int i1 = kNoIndex;
+#pragma unroll
+  for (int grp = 0; grp < kVB * 4; ++grp) {
+    const int v0 = vbase + (grp >> 2) * 32 + 8 * (grp & 3) + 4 * half;
+    const Philox4 pw = philox4x32_10((uint32_t)v0 >> 2, pabs, gstep, 0u, key0, key1);
+    const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {   // top two, first index on ties
+      const int i = 4 * grp + e;
+      const float y = __fmul_rn(z[i >> 4][i & 15], c2) + gumbel_bits(words[e]);
+      y2 = fmaxf(y2, fminf(y, y1));
+      i1 = y > y1 ? v0 + e : i1;
+      y1 = fmaxf(y1, y);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  Rec loc;
+  loc.m = m; loc.S = S; loc.A = A; loc.am = am;
+  loc.y1 = y1; loc.i1 = i1; loc.y2 = y2; loc.pad = 0.f;
+  const Rec oth = rec_shfl_xor(loc, 32);
+  return rec_merge(rec_pick(half == 0, loc, oth), rec_pick(half == 0, oth, loc));
+}
+
 // ---------------------------------------------------------------------------
 // k_project: fused projection + tempered softmax-entropy / argmax / Gumbel-max
 // ---------------------------------------------------------------------------
@@ -376,65 +442,7 @@ k_project(const ProjArgs a) {
         }
       }
 
-      // Tempered logits in bits: x = z * c2, recomputed in each pass rather
-      // than kept (registers are the scarce resource here).  The multiply is
-      // never fused with the following add, so every pass sees the same x.
-      // value index i = vb*16 + 4q + e  <->  vocabulary id vbase + vb*32 + 8q + 4h + e.
-      // In a ragged last tile, ids past V get the logit kMasked, far below
-      // the running-max start kNeg: they add exact zeros to S and A and never
-      // win the argmax or the sample.
-      const float c2 = a.c2;
-      if (vbase + kVocabPerWave > a.V) {
-#pragma unroll
-        for (int i = 0; i < kVB * 16; ++i) {
-          const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
-          z[i >> 4][i & 15] = v < a.V ? z[i >> 4][i & 15] : kMasked / c2;
-        }
-      }
-      float m = kNeg;
-      int am = kNoIndex;
-#pragma unroll
-      for (int i = 0; i < kVB * 16; ++i) {   // first maximum (ids increase with i)
-        const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
-        const float x = __fmul_rn(z[i >> 4][i & 15], c2);
-        am = x > m ? v : am;
-        m = fmaxf(m, x);
-      }
-      // Scheduling barriers bound how far the scheduler may hoist work across
-      // the value loops: unbounded, it keeps every intermediate of the block
-      // live at once and spills.
-      __builtin_amdgcn_sched_barrier(0);
-      float S = 0.f, A = 0.f;
-#pragma unroll
-      for (int i = 0; i < kVB * 16; ++i) {
-        const float dx = __fmul_rn(z[i >> 4][i & 15], c2) - m;
-        const float e = fexp2(dx);
-        S += e;
-        A = fmaf(dx, e, A);
-        if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
-      }
-      float y1 = kNeg, y2 = kNeg;
-      int i1 = kNoIndex;
-#pragma unroll
-      for (int grp = 0; grp < kVB * 4; ++grp) {
-        const int v0 = vbase + (grp >> 2) * 32 + 8 * (grp & 3) + 4 * half;
-        const Philox4 pw = philox4x32_10((uint32_t)v0 >> 2, pabs, (uint32_t)a.gstep, 0u, key0, key1);
-        const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {   // top two, first index on ties
-          const int i = 4 * grp + e;
-          const float y = __fmul_rn(z[i >> 4][i & 15], c2) + gumbel_bits(words[e]);
-          y2 = fmaxf(y2, fminf(y, y1));
-          i1 = y > y1 ? v0 + e : i1;
-          y1 = fmaxf(y1, y);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      Rec loc;
-      loc.m = m; loc.S = S; loc.A = A; loc.am = am;
-      loc.y1 = y1; loc.i1 = i1; loc.y2 = y2; loc.pad = 0.f;
-      const Rec oth = rec_shfl_xor(loc, 32);
-      const Rec wrec = rec_merge(rec_pick(half == 0, loc, oth), rec_pick(half == 0, oth, loc));
+      const Rec wrec = tile_record(z, vbase, half, a.V, a.c2, pabs, (uint32_t)a.gstep, key0, key1);
       if (half == 0) {
         Rec* slot = recs + wave * PPW + pb * 32 + col;
         rec_store(slot, rec_merge(rec_load(slot), wrec));
@@ -449,6 +457,266 @@ k_project(const ProjArgs a) {
     Rec r = rec_load(recs + (gp * kVGroups) * PPW + lp);
 #pragma unroll
     for (int w = 1; w < kVGroups; ++w) r = rec_merge(r, rec_load(recs + (gp * kVGroups + w) * PPW + lp));
+    const int row = row0 + t;
+    if (row < a.M) rec_store(a.part + (size_t)row * a.P + g, r);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Packed vocabulary table and the projection kernel that streams it
+// ---------------------------------------------------------------------------
+// dgd_pack_vocab() rewrites W [V][d] once into MFMA fragment order, so that
+// every 128-bit load of the projection reads 1 KB of contiguous memory and
+// lands directly in the A-operand registers (no LDS staging of W):
+//   64-row group rg, 64-element hidden chunk c, MFMA step s (0..3),
+//   32-row fragment f (0..1), lane l (0..63), element j (0..7)  ->
+//   W[64 rg + 32 f + l%32][64 c + 32 (l/32) + 8 s + j]
+// (the hidden-index permutation 32h + 8s + j is the one the H fragments use,
+// so the summed products are exactly those of the plain dot product).  Rows
+// past V and hidden elements past d are stored as zeros.
+constexpr int kPackRows = 64;
+constexpr uint32_t kPackChunkBytes = 8192;   // 4 steps x 2 fragments x 1 KB
+
+__host__ __device__ inline int packed_chunks(int d) { return (d + kKChunk - 1) / kKChunk; }
+__host__ __device__ inline int packed_groups(int V) { return (V + kPackRows - 1) / kPackRows; }
+
+__global__ void __launch_bounds__(kThreads) k_pack_vocab(const uint16_t* __restrict__ W,
+                                                         uint16_t* __restrict__ Wp, int V, int d,
+                                                         int nk, int64_t units) {
+  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (u >= units) return;
+  const int lane = (int)(u & 63);
+  const int f = (int)((u >> 6) & 1);
+  const int s = (int)((u >> 7) & 3);
+  const int64_t q = u >> 9;                      // rg * nk + c
+  const int c = (int)(q % nk);
+  const int64_t v = (q / nk) * kPackRows + 32 * f + (lane & 31);
+  const int k = c * kKChunk + 32 * (lane >> 5) + 8 * s;
+  u32x4_t val = {0u, 0u, 0u, 0u};
+  if (v < V && k < d) val = *(const u32x4_t*)(W + v * d + k);
+  *(u32x4_t*)(Wp + u * 8) = val;
+}
+
+// k_project_packed: the projection over a packed table.  Workgroup = 4 waves,
+// one per SIMD (512 registers each), one workgroup per CU.  Tile = 256
+// vocabulary rows x MROWS = 32*NB positions; wave w owns vocabulary rows
+// 64w .. 64w+63 of the tile against ALL positions of the tile, so each W
+// fragment is loaded by exactly one wave and feeds 2*NB MFMAs, and the 256
+// accumulator registers of a 64 x 256 wave tile live in AGPRs.
+//
+// K loop, per 64-element hidden chunk c: the H chunk (L2-resident) is staged
+// through double-buffered, swizzled LDS as in k_project; W fragments of chunk
+// c+2 are loaded straight into the registers that chunk c's MFMAs have just
+// consumed (a two-chunk register ring).  The stream does not stop at a tile
+// boundary: the last two loads of a tile fetch chunks 0 and 1 of the
+// workgroup's next tile, and the H chunk after the last one is chunk 0 again,
+// so the next tile's K loop starts with its operands in flight.  Chunks past
+// the end (odd chunk counts, past the last tile) read zeros without a memory
+// access.
+template <int NB, bool kLogits, bool kUniformKey>
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_project_packed(const ProjArgs a) {
+  static_assert(NB == 1 || NB == 2 || NB == 4 || NB == 8, "NB");
+  constexpr int MROWS = 32 * NB;
+  constexpr int HSEG = MROWS * (kKChunk / 8) / kThreads;   // 16-byte H segments per thread
+  constexpr int HBUF = MROWS * kKChunk * 2;
+  static_assert(HSEG == NB, "tiling");
+  __shared__ __attribute__((aligned(16))) uint8_t hsm[2 * HBUF];
+  __shared__ __attribute__((aligned(16))) Rec recs[kWaves * MROWS];
+
+  const int tid = threadIdx.x;
+  // the wave index is uniform: keep it (and the buffer resources built from
+  // it) in scalar registers
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+
+  if (blockIdx.x == 0 && tid < a.B) a.counters[tid] = 0;
+
+  int mt, g;
+  tile_of_block(blockIdx.x, a.n_mtiles, a.P, mt, g);
+  const int row0 = mt * MROWS;
+  {
+    const int last_row = min(row0 + MROWS, a.M) - 1;
+    bool all_done = true;
+    for (int c = row0 / a.L; c <= last_row / a.L; ++c) all_done &= (a.done[c] != 0);
+    if (all_done) return;
+  }
+  for (int i = tid; i < kWaves * MROWS; i += kThreads) rec_store(recs + i, rec_empty());
+
+  const int nk = packed_chunks(a.d);
+  const int nk2 = (nk + 1) & ~1;
+  const size_t d = (size_t)a.d;
+  const uint32_t rg_bytes = (uint32_t)nk * kPackChunkBytes;
+  const int n_rg = packed_groups(a.V);
+
+  // W fragments of the wave's 64-row group in tile vt (empty past the end)
+  auto wres_of = [&](int vt) {
+    const int rg = vt * kWaves + wave;
+    const bool ok = vt < a.n_vtiles && rg < n_rg;
+    return __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.W + (ok ? (size_t)rg * (rg_bytes / 2) : 0)), (short)0, ok ? (int)rg_bytes : 0,
+        kRsrcWord3);
+  };
+  const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.H + (size_t)row0 * d), (short)0, (int)((size_t)min(MROWS, a.M - row0) * d * 2),
+      kRsrcWord3);
+  const uint32_t hoff = (uint32_t)((tid >> 3) * d * 2 + (tid & 7) * 16);
+  const uint32_t hstride = (uint32_t)((kThreads / 8) * d * 2);      // 32 rows
+  const uint32_t lane_off = (uint32_t)lane * 16;
+
+  auto load_h = [&](int c, u32x4_t (&dst)[HSEG]) {
+    const uint32_t oob = (uint32_t)(c * kKChunk + (tid & 7) * 8 >= a.d) << 31;
+#pragma unroll
+    for (int i = 0; i < HSEG; ++i) {
+      const uint32_t off = (hoff + (uint32_t)i * hstride + (uint32_t)(c * kKChunk * 2)) | oob;
+      dst[i] = __builtin_amdgcn_raw_buffer_load_b128(hres, off, 0, 0);
+    }
+  };
+  auto store_h = [&](int buf, const u32x4_t (&src)[HSEG]) {
+    uint8_t* base = hsm + buf * HBUF;
+#pragma unroll
+    for (int i = 0; i < HSEG; ++i) {
+      const int idx = i * kThreads + tid;
+      const int r = idx >> 3, e = idx & 7;
+      *(u32x4_t*)(base + r * 128 + ((e ^ swz(r)) << 4)) = src[i];
+    }
+  };
+
+  u32x4_t wx[8], wy[8], hs[HSEG];
+  __amdgpu_buffer_rsrc_t wcur = wres_of(g), wnext = wres_of(g + a.P);
+  // prologue: chunks 0 and 1 of the first tile, H chunk 0
+  {
+    const uint32_t oob1 = (uint32_t)(1 >= nk) << 31;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      wx[j] = __builtin_amdgcn_raw_buffer_load_b128(wcur, lane_off + (uint32_t)j * 1024u, 0, kNonTemporal);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      wy[j] = __builtin_amdgcn_raw_buffer_load_b128(
+          wcur, (kPackChunkBytes + lane_off + (uint32_t)j * 1024u) | oob1, 0, kNonTemporal);
+    load_h(0, hs);
+    store_h(0, hs);
+  }
+
+  for (int vt = g; vt < a.n_vtiles; vt += a.P) {
+    const int vbase = vt * kVocabTile + wave * kVocabPerWave;
+
+    f32x16_t acc[kVB][NB];
+#pragma unroll
+    for (int vb = 0; vb < kVB; ++vb)
+#pragma unroll
+      for (int pb = 0; pb < NB; ++pb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[vb][pb][i] = 0.f;
+
+    __syncthreads();   // H chunk 0 is in buffer 0; the previous tile's records are merged
+
+    // One chunk: MFMAs on H buffer c&1 and W registers wreg (chunk c); the
+    // loads of H(c+1) are issued first and those of W(c+2) after them, step
+    // by step into the registers just consumed (vmcnt retires loads in
+    // order, so the wait for H at the end of the chunk leaves W in flight).
+    auto chunk = [&](int c, u32x4_t (&wreg)[8], u32x4_t (&hs_)[HSEG]) {
+      const int hnext = c + 1 < nk2 ? c + 1 : 0;
+      const int cw = c + 2;
+      const bool to_next = cw >= nk2;
+      const __amdgpu_buffer_rsrc_t wr = to_next ? wnext : wcur;
+      const int cl = to_next ? cw - nk2 : cw;
+      const uint32_t woob = (uint32_t)(cl >= nk) << 31;
+      const uint32_t wbase = (uint32_t)cl * kPackChunkBytes + lane_off;
+      __builtin_amdgcn_sched_barrier(0);
+      load_h(hnext, hs_);
+      __builtin_amdgcn_sched_barrier(0);
+      const uint8_t* hb = hsm + (c & 1) * HBUF;
+      bf16x8_t bf[2][NB];
+      auto load_b = [&](int s, bf16x8_t (&dst)[NB]) {
+        const int e = (4 * half + s) ^ swz(col);
+#pragma unroll
+        for (int pb = 0; pb < NB; ++pb)
+          dst[pb] = as_bf16x8(*(const u32x4_t*)(hb + (pb * 32 + col) * 128 + (e << 4)));
+      };
+      // Issue order per step s, pinned by scheduling barriers: the B
+      // fragments of step s+1 (so their LDS latency hides under this step's
+      // MFMAs), the 2*NB MFMAs of step s, then the W loads of chunk c+2 into
+      // the two registers those MFMAs have consumed.
+      load_b(0, bf[0]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (s < 3) load_b(s + 1, bf[(s + 1) & 1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const bf16x8_t a0 = as_bf16x8(wreg[2 * s]), a1 = as_bf16x8(wreg[2 * s + 1]);
+#pragma unroll
+        for (int pb = 0; pb < NB; ++pb) {
+          acc[0][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bf[s & 1][pb], acc[0][pb], 0, 0, 0);
+          acc[1][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bf[s & 1][pb], acc[1][pb], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wreg[2 * s] = __builtin_amdgcn_raw_buffer_load_b128(
+            wr, (wbase + (uint32_t)(2 * s) * 1024u) | woob, 0, kNonTemporal);
+        wreg[2 * s + 1] = __builtin_amdgcn_raw_buffer_load_b128(
+            wr, (wbase + (uint32_t)(2 * s + 1) * 1024u) | woob, 0, kNonTemporal);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      store_h((c + 1) & 1, hs_);
+      __syncthreads();
+    };
+    for (int c = 0; c < nk2; c += 2) {
+      chunk(c, wx, hs);
+      chunk(c + 1, wy, hs);
+    }
+    wcur = wnext;
+    wnext = wres_of(vt + 2 * a.P);
+
+    // ---------------- epilogue: one position per lane per block ----------
+#pragma unroll 1
+    for (int pb = 0; pb < NB; ++pb) {
+      f32x16_t z[kVB];
+      switch (pb) {
+#define DGD_TAKE(P)                                            \
+  case P:                                                      \
+    _Pragma("unroll") for (int vb = 0; vb < kVB; ++vb)         \
+        z[vb] = acc[vb][(P) < NB ? (P) : 0];                   \
+    break;
+        DGD_TAKE(0) DGD_TAKE(1) DGD_TAKE(2) DGD_TAKE(3)
+        DGD_TAKE(4) DGD_TAKE(5) DGD_TAKE(6) DGD_TAKE(7)
+#undef DGD_TAKE
+      }
+      const int r = row0 + pb * 32 + col;
+      const bool rvalid = r < a.M;
+      int cv = rvalid ? r / a.L : 0;
+      if constexpr (kUniformKey) cv = __builtin_amdgcn_readfirstlane(cv);
+      const int p = r - cv * a.L;
+      const uint32_t pabs = (uint32_t)(a.block * a.L + p);
+      const uint32_t key0 = a.key[cv][0], key1 = a.key[cv][1];
+
+      if constexpr (kLogits) {
+        if (rvalid) {
+#pragma unroll
+          for (int vb = 0; vb < kVB; ++vb)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int v0 = vbase + vb * 32 + 8 * q + 4 * half;
+              float* dst = a.logits + (size_t)r * a.V + v0;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (v0 + e < a.V) dst[e] = z[vb][4 * q + e];
+            }
+        }
+      }
+      const Rec wrec = tile_record(z, vbase, half, a.V, a.c2, pabs, (uint32_t)a.gstep, key0, key1);
+      if (half == 0) {
+        Rec* slot = recs + wave * MROWS + pb * 32 + col;
+        rec_store(slot, rec_merge(rec_load(slot), wrec));
+      }
+    }
+  }
+
+  // ------- merge the four vocabulary waves of each position (fixed order) -------
+  __syncthreads();
+  for (int t = tid; t < MROWS; t += kThreads) {
+    Rec r = rec_load(recs + t);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = rec_merge(r, rec_load(recs + w * MROWS + t));
     const int row = row0 + t;
     if (row < a.M) rec_store(a.part + (size_t)row * a.P + g, r);
   }
@@ -759,8 +1027,13 @@ int check_shape(const dgd_ctx* ctx) {
     return fail(DGD_EUNSUPPORTED, "d=%d must be a multiple of 8 in [8, %d]", ctx->d,
                 DGD_MAX_HIDDEN);
   if (!ctx->state) return fail(DGD_EINVAL, "ctx->state is NULL");
+  if (ctx->vocab_layout != DGD_VOCAB_ROWS && ctx->vocab_layout != DGD_VOCAB_PACKED)
+    return fail(DGD_EINVAL, "vocab_layout=%d is neither DGD_VOCAB_ROWS nor DGD_VOCAB_PACKED",
+                ctx->vocab_layout);
   return DGD_OK;
 }
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
 int check_params(const dgd_params* prm) {
   if (!prm) return fail(DGD_EINVAL, "params is NULL");
@@ -872,6 +1145,17 @@ void launch_project_mb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits,
   }
 }
 
+template <int NB>
+void launch_packed_nb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits, bool uniform) {
+  if (logits) {
+    if (uniform) hipLaunchKernelGGL((k_project_packed<NB, true, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_project_packed<NB, true, false>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (uniform) hipLaunchKernelGGL((k_project_packed<NB, false, true>), grid, dim3(kThreads), 0, s, a);
+    else hipLaunchKernelGGL((k_project_packed<NB, false, false>), grid, dim3(kThreads), 0, s, a);
+  }
+}
+
 int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* committed,
                 int block, int step, const dgd_params* prm, const uint64_t* seed,
                 const dgd_ctx* ctx, Timer& timer) {
@@ -897,17 +1181,30 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   pa.block = block; pa.gstep = gstep;
   pa.c2 = (float)(kLog2e / T);
   fill_keys(pa.key, seed, B);
-  const int MB = M <= 64 ? 2 : M <= 128 ? 4 : 8;
-  pa.n_mtiles = (M + 32 * MB - 1) / (32 * MB);
-  const dim3 grid1(pa.n_mtiles * pa.P);
-  int rc = timer.begin(stream);
-  if (rc) return rc;
   const bool lg = ctx->logits != nullptr;
   const bool uni = (L % 32) == 0;
-  switch (MB) {
-    case 2: launch_project_mb<2>(pa, grid1, stream, lg, uni); break;
-    case 4: launch_project_mb<4>(pa, grid1, stream, lg, uni); break;
-    default: launch_project_mb<8>(pa, grid1, stream, lg, uni); break;
+  int rc;
+  if (ctx->vocab_layout == DGD_VOCAB_PACKED) {
+    const int NB = M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8;
+    pa.n_mtiles = (M + 32 * NB - 1) / (32 * NB);
+    const dim3 grid1(pa.n_mtiles * pa.P);
+    if ((rc = timer.begin(stream))) return rc;
+    switch (NB) {
+      case 1: launch_packed_nb<1>(pa, grid1, stream, lg, uni); break;
+      case 2: launch_packed_nb<2>(pa, grid1, stream, lg, uni); break;
+      case 4: launch_packed_nb<4>(pa, grid1, stream, lg, uni); break;
+      default: launch_packed_nb<8>(pa, grid1, stream, lg, uni); break;
+    }
+  } else {
+    const int MB = M <= 64 ? 2 : M <= 128 ? 4 : 8;
+    pa.n_mtiles = (M + 32 * MB - 1) / (32 * MB);
+    const dim3 grid1(pa.n_mtiles * pa.P);
+    if ((rc = timer.begin(stream))) return rc;
+    switch (MB) {
+      case 2: launch_project_mb<2>(pa, grid1, stream, lg, uni); break;
+      case 4: launch_project_mb<4>(pa, grid1, stream, lg, uni); break;
+      default: launch_project_mb<8>(pa, grid1, stream, lg, uni); break;
+    }
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "k_project launch");
@@ -982,6 +1279,7 @@ int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_
   if ((rc = check_knobs(ctx, seed, true))) return rc;
   if ((rc = check_workspace(ctx))) return rc;
   if (!H || !W_vocab || !canvas || !committed) return fail(DGD_EINVAL, "H/W_vocab/canvas/committed is NULL");
+  if (!aligned16(H) || !aligned16(W_vocab)) return fail(DGD_EINVAL, "H/W_vocab is not 16-byte aligned");
   if (block < 0 || block >= ctx->G / ctx->L)
     return fail(DGD_EINVAL, "block=%d outside [0, %d)", block, ctx->G / ctx->L);
   if (step < 0 || step >= params->num_inference_steps)
@@ -1003,6 +1301,8 @@ int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas, u
   if ((rc = check_workspace(ctx))) return rc;
   if (!H_steps || !W_vocab || !canvas || !committed)
     return fail(DGD_EINVAL, "H_steps/W_vocab/canvas/committed is NULL");
+  if (!aligned16(H_steps) || !aligned16(W_vocab))
+    return fail(DGD_EINVAL, "H_steps/W_vocab is not 16-byte aligned");
   const int N = params->num_inference_steps;
   const int blocks = ctx->G / ctx->L;
   const size_t step_elems = (size_t)ctx->B * ctx->L * ctx->d;
@@ -1016,6 +1316,31 @@ int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas, u
   }
   const int rt = timer.finish(ctx);
   return rc ? rc : rt;
+}
+
+size_t dgd_packed_vocab_bytes(int32_t V, int32_t d) {
+  if (V < 1 || V > DGD_MAX_VOCAB || d < 8 || d > DGD_MAX_HIDDEN || d % 8 != 0) return 0;
+  return (size_t)packed_groups(V) * kPackRows * (size_t)packed_chunks(d) * kKChunk * 2;
+}
+
+int dgd_pack_vocab(const dgd_bf16* W_vocab, dgd_bf16* W_packed, int32_t V, int32_t d, void* stream) {
+  g_err.clear();
+  if (!W_vocab || !W_packed) return fail(DGD_EINVAL, "W_vocab/W_packed is NULL");
+  if (V < 1 || V > DGD_MAX_VOCAB) return fail(DGD_EUNSUPPORTED, "V=%d outside [1, 2^24]", V);
+  if (d < 8 || d > DGD_MAX_HIDDEN || d % 8 != 0)
+    return fail(DGD_EUNSUPPORTED, "d=%d must be a multiple of 8 in [8, %d]", d, DGD_MAX_HIDDEN);
+  if (!aligned16(W_vocab) || !aligned16(W_packed))
+    return fail(DGD_EINVAL, "W_vocab/W_packed is not 16-byte aligned");
+  const size_t bytes = dgd_packed_vocab_bytes(V, d);
+  const uintptr_t s0 = (uintptr_t)W_vocab, s1 = s0 + (size_t)V * d * 2;
+  const uintptr_t d0 = (uintptr_t)W_packed, d1 = d0 + bytes;
+  if (s0 < d1 && d0 < s1) return fail(DGD_EINVAL, "W_vocab and W_packed overlap");
+  const int64_t units = (int64_t)(bytes / 16);
+  const int64_t blocks = (units + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(k_pack_vocab, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream,
+                     W_vocab, W_packed, V, d, packed_chunks(d), units);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_pack_vocab launch");
 }
 
 int dgd_debug_gumbel(const uint32_t* words, float* out, int64_t n, void* stream) {

@@ -23,8 +23,11 @@ DGD_EHIP = -4
 DGD_MAX_CANVASES = 64
 DGD_MAX_CANVAS_LEN = 4096
 
+DGD_VOCAB_ROWS = 0
+DGD_VOCAB_PACKED = 1
+
 EXPORTED = ("dgd_state_bytes", "dgd_workspace_bytes", "dgd_init_block", "dgd_step", "dgd_run",
-            "dgd_debug_gumbel", "dgd_last_error")
+            "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_debug_gumbel", "dgd_last_error")
 
 
 class DgdError(RuntimeError):
@@ -62,6 +65,7 @@ class DgdCtx(ctypes.Structure):
         ("commit_step", ctypes.c_void_p),
         ("k1_ms", ctypes.POINTER(ctypes.c_double)),
         ("k1_launches", ctypes.POINTER(ctypes.c_int32)),
+        ("vocab_layout", ctypes.c_int32),
     ]
 
 
@@ -93,6 +97,11 @@ def load_library(path: str = LIB_PATH):
     lib.dgd_run.restype = ctypes.c_int
     lib.dgd_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                             pp, pseed, pc]
+    lib.dgd_packed_vocab_bytes.restype = ctypes.c_size_t
+    lib.dgd_packed_vocab_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.dgd_pack_vocab.restype = ctypes.c_int
+    lib.dgd_pack_vocab.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p]
     lib.dgd_debug_gumbel.restype = ctypes.c_int
     lib.dgd_debug_gumbel.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                      ctypes.c_void_p]
@@ -142,7 +151,7 @@ class Context:
     """
 
     def __init__(self, B, L, V, d, G, bounds, device="cuda", outputs=True, logits=False,
-                 commit_trace=False):
+                 commit_trace=False, vocab_layout=DGD_VOCAB_ROWS):
         import torch
         lib = load_library()
         self.B, self.L, self.V, self.d, self.G = int(B), int(L), int(V), int(d), int(G)
@@ -168,6 +177,7 @@ class Context:
         self._k1_ms = ctypes.c_double(0.0)
         self._k1_n = ctypes.c_int32(0)
         self.time_k1 = False
+        self.vocab_layout = int(vocab_layout)
 
     def state_views(self) -> dict:
         B, BL = self.B, self.B * self.L
@@ -201,6 +211,7 @@ class Context:
         c.gap = _ptr(self.gap)
         c.logits = _ptr(self.logits)
         c.commit_step = _ptr(self.commit_step)
+        c.vocab_layout = self.vocab_layout
         if self.time_k1:
             c.k1_ms = ctypes.pointer(self._k1_ms)
             c.k1_launches = ctypes.pointer(self._k1_n)
@@ -242,6 +253,23 @@ def dgd_run(H_steps, W_vocab, canvas, committed, params: DgdParams, seeds, ctx: 
     _check(load_library().dgd_run(_ptr(H_steps, 2), _ptr(W_vocab, 2), _ptr(canvas, 4),
                                   _ptr(committed, 1), ctypes.byref(params), _seeds(seeds),
                                   ctypes.byref(c)))
+
+
+def dgd_packed_vocab_bytes(V: int, d: int) -> int:
+    return int(load_library().dgd_packed_vocab_bytes(V, d))
+
+
+def dgd_pack_vocab(W_vocab, W_packed, V: int, d: int, stream=None):
+    _check(load_library().dgd_pack_vocab(_ptr(W_vocab, 2), _ptr(W_packed, 2), int(V), int(d),
+                                         _stream_handle(stream)))
+
+
+def pack_vocab(W_vocab, V: int, d: int, stream=None):
+    """Packed copy of a device bf16 table (a new torch tensor of int16 words)."""
+    import torch
+    out = torch.empty(dgd_packed_vocab_bytes(V, d) // 2, dtype=torch.int16, device=W_vocab.device)
+    dgd_pack_vocab(W_vocab, out, V, d, stream)
+    return out
 
 
 def dgd_debug_gumbel(words, out, stream=None):
