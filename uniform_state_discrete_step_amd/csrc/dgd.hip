@@ -153,6 +153,12 @@ constexpr int kRsrcWord3 = 0x00020000;
 constexpr uint32_t kOOB = 0x80000000u;
 constexpr int kNonTemporal = 2;   // streaming (nt) cache policy for W
 
+// s_waitcnt immediate (gfx9 encoding): wait until at most `vm` vector-memory
+// and `lgkm` LDS/scalar operations of this wave are outstanding.
+constexpr int waitcnt_enc(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
+
 // Record of one position over the 64 vocabulary ids held by a lane pair:
 // z[vb][4q + e] (lane half h) is the logit of id vbase + 32 vb + 8 q + 4 h + e.
 // The two halves' records are merged; both lanes return the merged record.
@@ -521,7 +527,10 @@ k_project_packed(const ProjArgs a) {
   constexpr int HSEG = MROWS * (kKChunk / 8) / kThreads;   // 16-byte H segments per thread
   constexpr int HBUF = MROWS * kKChunk * 2;
   static_assert(HSEG == NB, "tiling");
-  __shared__ __attribute__((aligned(16))) uint8_t hsm[2 * HBUF];
+  // two H buffers as separate arrays: chunk c reads hbuf[c&1], and the
+  // compiler can tell reads of one from DMA writes into the other
+  __shared__ __attribute__((aligned(16))) uint8_t hsm0[HBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t hsm1[HBUF];
   __shared__ __attribute__((aligned(16))) Rec recs[kWaves * MROWS];
 
   const int tid = threadIdx.x;
@@ -560,31 +569,46 @@ k_project_packed(const ProjArgs a) {
   const __amdgpu_buffer_rsrc_t hres = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.H + (size_t)row0 * d), (short)0, (int)((size_t)min(MROWS, a.M - row0) * d * 2),
       kRsrcWord3);
-  const uint32_t hoff = (uint32_t)((tid >> 3) * d * 2 + (tid & 7) * 16);
-  const uint32_t hstride = (uint32_t)((kThreads / 8) * d * 2);      // 32 rows
   const uint32_t lane_off = (uint32_t)lane * 16;
 
-  auto load_h = [&](int c, u32x4_t (&dst)[HSEG]) {
-    const uint32_t oob = (uint32_t)(c * kKChunk + (tid & 7) * 8 >= a.d) << 31;
+  // H chunks reach LDS by DMA (buffer_load ... lds): instruction i of wave w
+  // fills rows (i*kWaves + w)*8 .. +7 of an H buffer, lane l writing slot l%8
+  // of row l/8, so that slot holds hidden segment (l%8) ^ swz(row).  Rows past
+  // M re-read row M-1 and segments past d re-read segment 0 of their row: no
+  // access leaves H, and the packed W is zero at those hidden indices, so they
+  // add exact zeros (their rows are never stored).
+  const int hseg = (lane & 7) ^ swz((lane >> 3) + 8 * (wave & 1));
+  const int last_rel = a.M - 1 - row0;
+  const uint32_t d2 = (uint32_t)(d * 2);
+  // The DMA is written as inline assembly on purpose: the compiler's wait
+  // insertion treats a pending LDS DMA as making the vector-memory counter
+  // unordered and then waits for every load in flight (vmcnt(0)) before the
+  // next use of a W register, which drains the W prefetch.  The waits the
+  // DMA needs are explicit in the K loop instead (vmcnt before each barrier).
+  auto dma_h = [&](int c, uint8_t* hbuf) {
+    const uint32_t koff = c * kKChunk + hseg * 8 < a.d ? (uint32_t)(c * kKChunk * 2) : 0u - (uint32_t)hseg * 16;
+    const uint32_t lbase =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)hbuf + (uint32_t)wave * 1024u;
 #pragma unroll
     for (int i = 0; i < HSEG; ++i) {
-      const uint32_t off = (hoff + (uint32_t)i * hstride + (uint32_t)(c * kKChunk * 2)) | oob;
-      dst[i] = __builtin_amdgcn_raw_buffer_load_b128(hres, off, 0, 0);
+      const int r = min((i * kWaves + wave) * 8 + (lane >> 3), last_rel);
+      const uint32_t off = (uint32_t)r * d2 + (uint32_t)hseg * 16 + koff;
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                   :
+                   : "v"(off), "s"(hres), "{m0}"(lbase + (uint32_t)(i * kWaves * 1024)));
     }
   };
-  auto store_h = [&](int buf, const u32x4_t (&src)[HSEG]) {
-    uint8_t* base = hsm + buf * HBUF;
-#pragma unroll
-    for (int i = 0; i < HSEG; ++i) {
-      const int idx = i * kThreads + tid;
-      const int r = idx >> 3, e = idx & 7;
-      *(u32x4_t*)(base + r * 128 + ((e ^ swz(r)) << 4)) = src[i];
-    }
+  // B fragment pb of MFMA step s from an H buffer
+  auto read_b = [&](const uint8_t* hb, int s, int pb) {
+    const int e = (4 * half + s) ^ swz(col);
+    return as_bf16x8(*(const u32x4_t*)(hb + (pb * 32 + col) * 128 + (e << 4)));
   };
 
-  u32x4_t wx[8], wy[8], hs[HSEG];
+  u32x4_t wx[8], wy[8];
+  bf16x8_t bfr[NB];   // B fragments of the step in progress
   __amdgpu_buffer_rsrc_t wcur = wres_of(g), wnext = wres_of(g + a.P);
-  // prologue: chunks 0 and 1 of the first tile, H chunk 0
+  // prologue: W chunks 0 and 1 of the first tile, H chunks 0 and 1, and the
+  // B fragments of step 0
   {
     const uint32_t oob1 = (uint32_t)(1 >= nk) << 31;
 #pragma unroll
@@ -594,8 +618,10 @@ k_project_packed(const ProjArgs a) {
     for (int j = 0; j < 8; ++j)
       wy[j] = __builtin_amdgcn_raw_buffer_load_b128(
           wcur, (kPackChunkBytes + lane_off + (uint32_t)j * 1024u) | oob1, 0, kNonTemporal);
-    load_h(0, hs);
-    store_h(0, hs);
+    dma_h(0, hsm0);
+    dma_h(1 < nk ? 1 : 0, hsm1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_enc(0, 0));
+    __syncthreads();
   }
 
   for (int vt = g; vt < a.n_vtiles; vt += a.P) {
@@ -609,60 +635,81 @@ k_project_packed(const ProjArgs a) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[vb][pb][i] = 0.f;
 
-    __syncthreads();   // H chunk 0 is in buffer 0; the previous tile's records are merged
-
-    // One chunk: MFMAs on H buffer c&1 and W registers wreg (chunk c); the
-    // loads of H(c+1) are issued first and those of W(c+2) after them, step
-    // by step into the registers just consumed (vmcnt retires loads in
-    // order, so the wait for H at the end of the chunk leaves W in flight).
-    auto chunk = [&](int c, u32x4_t (&wreg)[8], u32x4_t (&hs_)[HSEG]) {
-      const int hnext = c + 1 < nk2 ? c + 1 : 0;
+    // One chunk c (LDS buffer hcur, W registers wreg).  Per MFMA step s the
+    // issue order is pinned by scheduling barriers: for each B fragment, its
+    // two MFMAs and then the LDS read of the same fragment of step s+1 into
+    // the register just consumed; then the two W loads of chunk c+2 into the
+    // W registers of step s.  Step 3 is split around the chunk's only
+    // barrier: the first half of its MFMAs, a wait for this wave's DMA of
+    // H(c+1) (vmcnt retires in order; the eight W loads issued after it may
+    // stay in flight) and for its LDS reads, the barrier, then the reads of
+    // step 0 of chunk c+1 and the DMA of H(c+2) into the buffer just
+    // released, then the rest.  The stream runs on into the next tile: W
+    // chunk c+2 past the end is chunk c+2-nk2 of the next tile, and H is the
+    // same for every tile of the workgroup.
+    auto chunk = [&](int c, u32x4_t (&wreg)[8], uint8_t* hcur, uint8_t* hoth) {
       const int cw = c + 2;
       const bool to_next = cw >= nk2;
       const __amdgpu_buffer_rsrc_t wr = to_next ? wnext : wcur;
       const int cl = to_next ? cw - nk2 : cw;
       const uint32_t woob = (uint32_t)(cl >= nk) << 31;
       const uint32_t wbase = (uint32_t)cl * kPackChunkBytes + lane_off;
-      __builtin_amdgcn_sched_barrier(0);
-      load_h(hnext, hs_);
-      __builtin_amdgcn_sched_barrier(0);
-      const uint8_t* hb = hsm + (c & 1) * HBUF;
-      bf16x8_t bf[2][NB];
-      auto load_b = [&](int s, bf16x8_t (&dst)[NB]) {
-        const int e = (4 * half + s) ^ swz(col);
-#pragma unroll
-        for (int pb = 0; pb < NB; ++pb)
-          dst[pb] = as_bf16x8(*(const u32x4_t*)(hb + (pb * 32 + col) * 128 + (e << 4)));
-      };
-      // Issue order per step s, pinned by scheduling barriers: the B
-      // fragments of step s+1 (so their LDS latency hides under this step's
-      // MFMAs), the 2*NB MFMAs of step s, then the W loads of chunk c+2 into
-      // the two registers those MFMAs have consumed.
-      load_b(0, bf[0]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (s < 3) load_b(s + 1, bf[(s + 1) & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+      const int hc2 = cl < nk ? cl : 0;   // H chunk c+2 (any valid chunk for a phantom one)
+      auto mfma2 = [&](int s, int pb) {
         const bf16x8_t a0 = as_bf16x8(wreg[2 * s]), a1 = as_bf16x8(wreg[2 * s + 1]);
-#pragma unroll
-        for (int pb = 0; pb < NB; ++pb) {
-          acc[0][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bf[s & 1][pb], acc[0][pb], 0, 0, 0);
-          acc[1][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bf[s & 1][pb], acc[1][pb], 0, 0, 0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+        acc[0][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfr[pb], acc[0][pb], 0, 0, 0);
+        acc[1][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bfr[pb], acc[1][pb], 0, 0, 0);
+      };
+      auto wload = [&](int s) {
         wreg[2 * s] = __builtin_amdgcn_raw_buffer_load_b128(
             wr, (wbase + (uint32_t)(2 * s) * 1024u) | woob, 0, kNonTemporal);
         wreg[2 * s + 1] = __builtin_amdgcn_raw_buffer_load_b128(
             wr, (wbase + (uint32_t)(2 * s + 1) * 1024u) | woob, 0, kNonTemporal);
+      };
+#pragma unroll
+      for (int s = 0; s < 3; ++s) {
+#pragma unroll
+        for (int pb = 0; pb < NB; ++pb) {
+          __builtin_amdgcn_sched_barrier(0);
+          mfma2(s, pb);
+          __builtin_amdgcn_sched_barrier(0);
+          bfr[pb] = read_b(hcur, s + 1, pb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wload(s);
+      }
+#pragma unroll
+      for (int pb = 0; pb < NB / 2; ++pb) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma2(3, pb);
       }
       __builtin_amdgcn_sched_barrier(0);
-      store_h((c + 1) & 1, hs_);
+      __builtin_amdgcn_s_waitcnt(waitcnt_enc(8, 0));
       __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int pb = 0; pb < NB / 2; ++pb) bfr[pb] = read_b(hoth, 0, pb);
+      __builtin_amdgcn_sched_barrier(0);
+      dma_h(hc2, hcur);
+#pragma unroll
+      for (int pb = NB / 2; pb < NB; ++pb) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma2(3, pb);
+        __builtin_amdgcn_sched_barrier(0);
+        bfr[pb] = read_b(hoth, 0, pb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      wload(3);
+      __builtin_amdgcn_sched_barrier(0);
     };
+    // step-0 fragments of chunk 0 (H chunk 0 is in hsm0: loaded in the
+    // prologue or by the previous tile's stream, which waited for it); read
+    // here rather than carried through the epilogue, where registers are short
+#pragma unroll
+    for (int pb = 0; pb < NB; ++pb) bfr[pb] = read_b(hsm0, 0, pb);
     for (int c = 0; c < nk2; c += 2) {
-      chunk(c, wx, hs);
-      chunk(c + 1, wy, hs);
+      chunk(c, wx, hsm0, hsm1);
+      chunk(c + 1, wy, hsm1, hsm0);
     }
     wcur = wnext;
     wnext = wres_of(vt + 2 * a.P);
