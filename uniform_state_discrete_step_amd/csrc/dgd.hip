@@ -503,40 +503,54 @@ __global__ void __launch_bounds__(kThreads) k_pack_vocab(const uint16_t* __restr
   *(u32x4_t*)(Wp + u * 8) = val;
 }
 
-// k_project_packed: the projection over a packed table.  Workgroup = 4 waves,
-// one per SIMD (512 registers each), one workgroup per CU.  Tile = 256
-// vocabulary rows x MROWS = 32*NB positions; wave w owns vocabulary rows
-// 64w .. 64w+63 of the tile against ALL positions of the tile, so each W
-// fragment is loaded by exactly one wave and feeds 2*NB MFMAs, and the 256
-// accumulator registers of a 64 x 256 wave tile live in AGPRs.
+// k_project_packed: the projection over a packed table.  Tile = 256
+// vocabulary rows x MROWS = 32*NB positions, one workgroup per CU, 4*PW
+// waves (PW per SIMD).  Wave w owns vocabulary rows 64*(w%4) .. +63 of the
+// tile against positions (w/4)*PPW .. +PPW-1 (PPW = MROWS/PW): 2 x NBW MFMA
+// fragments, 32*NBW fp32 accumulators in AGPRs.  PW = 1 keeps one wave per
+// SIMD with 512 registers (each W fragment loaded once); PW = 2 runs two
+// waves per SIMD with 256 registers each (the two waves of a vocabulary group
+// load the same W fragments, the second from cache).
 //
-// K loop, per 64-element hidden chunk c: the H chunk (L2-resident) is staged
-// through double-buffered, swizzled LDS as in k_project; W fragments of chunk
-// c+2 are loaded straight into the registers that chunk c's MFMAs have just
-// consumed (a two-chunk register ring).  The stream does not stop at a tile
-// boundary: the last two loads of a tile fetch chunks 0 and 1 of the
-// workgroup's next tile, and the H chunk after the last one is chunk 0 again,
-// so the next tile's K loop starts with its operands in flight.  Chunks past
-// the end (odd chunk counts, past the last tile) read zeros without a memory
-// access.
-template <int NB, bool kLogits, bool kUniformKey>
-__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// K loop, per 64-element hidden chunk c:
+//   * W: fragments go straight from memory into a ring of RING chunks of
+//     registers; the loads of chunk c+RING are issued as chunk c's MFMAs free
+//     their registers.  Chunks at or past nk read zeros without a memory
+//     access (the loop is padded to whole rings).
+//   * H: chunk c+HB reaches LDS by DMA (buffer_load ... lds) into the buffer
+//     chunk c has just finished with; HB buffers, swizzled rows.
+//   * one barrier per chunk, inside MFMA step 3 (see chunk()).
+// The H stream is cyclic over the chunks, so a tile finds the first HB chunks
+// of H already in LDS.
+template <int NB, bool kLogits, bool kUniformKey, int PW, int RING, int HB>
+__global__ void __launch_bounds__(256 * PW) __attribute__((amdgpu_waves_per_eu(PW, PW)))
 k_project_packed(const ProjArgs a) {
   static_assert(NB == 1 || NB == 2 || NB == 4 || NB == 8, "NB");
-  constexpr int MROWS = 32 * NB;
-  constexpr int HSEG = MROWS * (kKChunk / 8) / kThreads;   // 16-byte H segments per thread
+  static_assert(PW == 1 || PW == 2, "PW");
+  constexpr int THREADS = 256 * PW;
+  constexpr int WAVES = 4 * PW;
+  constexpr int NBW = (NB >= PW) ? NB / PW : 1;      // B fragments per wave
+  constexpr int PPW = 32 * NBW;                       // positions per wave
+  constexpr int MROWS = PPW * PW;                     // positions per tile
+  constexpr int HSEG = MROWS * (kKChunk / 8) / THREADS;   // DMA loads per thread per chunk
   constexpr int HBUF = MROWS * kKChunk * 2;
-  static_assert(HSEG == NB, "tiling");
-  // two H buffers as separate arrays: chunk c reads hbuf[c&1], and the
-  // compiler can tell reads of one from DMA writes into the other
-  __shared__ __attribute__((aligned(16))) uint8_t hsm0[HBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t hsm1[HBUF];
-  __shared__ __attribute__((aligned(16))) Rec recs[kWaves * MROWS];
+  static_assert(HSEG >= 1 && HSEG * THREADS == MROWS * (kKChunk / 8), "tiling");
+  static_assert(RING % HB == 0, "the H buffer of a chunk must be static in the unrolled ring");
+  // VMEM operations a wave issues after its DMA of H(c+1) (step 3 of chunk
+  // c+1-HB, after the barrier) before it waits for it (step 3 of chunk c):
+  // the two W loads of that step 3, HB-2 whole chunks (8 W loads and HSEG
+  // DMA loads each) and the six W loads of steps 0-2 of chunk c.  Tile
+  // prologues only add loads after it, which keeps the wait sufficient.
+  constexpr int kDmaLag = 2 + (HB - 2) * (8 + HSEG) + 6;
+  static_assert(kDmaLag <= 63, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t hsm[HB][HBUF];
+  __shared__ __attribute__((aligned(16))) Rec recs[WAVES * PPW];
 
   const int tid = threadIdx.x;
-  // the wave index is uniform: keep it (and the buffer resources built from
-  // it) in scalar registers
+  // wave indices are uniform: keep them (and the buffer resources built from
+  // them) in scalar registers
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = wave & 3, wp = wave >> 2;
   const int lane = tid & 63, half = lane >> 5, col = lane & 31;
 
   if (blockIdx.x == 0 && tid < a.B) a.counters[tid] = 0;
@@ -550,17 +564,17 @@ k_project_packed(const ProjArgs a) {
     for (int c = row0 / a.L; c <= last_row / a.L; ++c) all_done &= (a.done[c] != 0);
     if (all_done) return;
   }
-  for (int i = tid; i < kWaves * MROWS; i += kThreads) rec_store(recs + i, rec_empty());
+  for (int i = tid; i < WAVES * PPW; i += THREADS) rec_store(recs + i, rec_empty());
 
   const int nk = packed_chunks(a.d);
-  const int nk2 = (nk + 1) & ~1;
+  const int nkr = (nk + RING - 1) / RING * RING;   // chunk loop padded to whole rings
   const size_t d = (size_t)a.d;
   const uint32_t rg_bytes = (uint32_t)nk * kPackChunkBytes;
   const int n_rg = packed_groups(a.V);
 
   // W fragments of the wave's 64-row group in tile vt (empty past the end)
   auto wres_of = [&](int vt) {
-    const int rg = vt * kWaves + wave;
+    const int rg = vt * 4 + wv;
     const bool ok = vt < a.n_vtiles && rg < n_rg;
     return __builtin_amdgcn_make_buffer_rsrc(
         (void*)(a.W + (ok ? (size_t)rg * (rg_bytes / 2) : 0)), (short)0, ok ? (int)rg_bytes : 0,
@@ -571,90 +585,90 @@ k_project_packed(const ProjArgs a) {
       kRsrcWord3);
   const uint32_t lane_off = (uint32_t)lane * 16;
 
-  // H chunks reach LDS by DMA (buffer_load ... lds): instruction i of wave w
-  // fills rows (i*kWaves + w)*8 .. +7 of an H buffer, lane l writing slot l%8
-  // of row l/8, so that slot holds hidden segment (l%8) ^ swz(row).  Rows past
-  // M re-read row M-1 and segments past d re-read segment 0 of their row: no
-  // access leaves H, and the packed W is zero at those hidden indices, so they
-  // add exact zeros (their rows are never stored).
-  const int hseg = (lane & 7) ^ swz((lane >> 3) + 8 * (wave & 1));
-  const int last_rel = a.M - 1 - row0;
-  const uint32_t d2 = (uint32_t)(d * 2);
+  // H chunks reach LDS by DMA: instruction i of wave w fills rows
+  // (i*WAVES + w)*8 .. +7 of an H buffer, lane l writing slot l%8 of row l/8,
+  // so that slot holds hidden segment (l%8) ^ swz(row).  Rows past M re-read
+  // row M-1 and segments past d re-read segment 0 of their row: no access
+  // leaves H, and the packed W is zero at those hidden indices, so they add
+  // exact zeros (their rows are never stored).
+  //
   // The DMA is written as inline assembly on purpose: the compiler's wait
   // insertion treats a pending LDS DMA as making the vector-memory counter
   // unordered and then waits for every load in flight (vmcnt(0)) before the
   // next use of a W register, which drains the W prefetch.  The waits the
   // DMA needs are explicit in the K loop instead (vmcnt before each barrier).
+  const int hseg = (lane & 7) ^ swz((lane >> 3) + 8 * (wave & 1));
+  const int last_rel = a.M - 1 - row0;
+  const uint32_t d2 = (uint32_t)(d * 2);
   auto dma_h = [&](int c, uint8_t* hbuf) {
     const uint32_t koff = c * kKChunk + hseg * 8 < a.d ? (uint32_t)(c * kKChunk * 2) : 0u - (uint32_t)hseg * 16;
     const uint32_t lbase =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)hbuf + (uint32_t)wave * 1024u;
 #pragma unroll
     for (int i = 0; i < HSEG; ++i) {
-      const int r = min((i * kWaves + wave) * 8 + (lane >> 3), last_rel);
+      const int r = min((i * WAVES + wave) * 8 + (lane >> 3), last_rel);
       const uint32_t off = (uint32_t)r * d2 + (uint32_t)hseg * 16 + koff;
       asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                    :
-                   : "v"(off), "s"(hres), "{m0}"(lbase + (uint32_t)(i * kWaves * 1024)));
+                   : "v"(off), "s"(hres), "{m0}"(lbase + (uint32_t)(i * WAVES * 1024)));
     }
   };
-  // B fragment pb of MFMA step s from an H buffer
+  // B fragment pb (of this wave's positions) of MFMA step s from an H buffer
   auto read_b = [&](const uint8_t* hb, int s, int pb) {
     const int e = (4 * half + s) ^ swz(col);
-    return as_bf16x8(*(const u32x4_t*)(hb + (pb * 32 + col) * 128 + (e << 4)));
+    return as_bf16x8(*(const u32x4_t*)(hb + (wp * PPW + pb * 32 + col) * 128 + (e << 4)));
   };
 
-  u32x4_t wx[8], wy[8];
-  bf16x8_t bfr[NB];   // B fragments of the step in progress
-  __amdgpu_buffer_rsrc_t wcur = wres_of(g), wnext = wres_of(g + a.P);
-  // prologue: W chunks 0 and 1 of the first tile, H chunks 0 and 1, and the
-  // B fragments of step 0
-  {
-    const uint32_t oob1 = (uint32_t)(1 >= nk) << 31;
+  bf16x8_t bfr[NBW];   // B fragments of the step in progress
+  // prologue: H chunks 0 .. HB-1 (later tiles find them already in place)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      wx[j] = __builtin_amdgcn_raw_buffer_load_b128(wcur, lane_off + (uint32_t)j * 1024u, 0, kNonTemporal);
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      wy[j] = __builtin_amdgcn_raw_buffer_load_b128(
-          wcur, (kPackChunkBytes + lane_off + (uint32_t)j * 1024u) | oob1, 0, kNonTemporal);
-    dma_h(0, hsm0);
-    dma_h(1 < nk ? 1 : 0, hsm1);
-    __builtin_amdgcn_s_waitcnt(waitcnt_enc(0, 0));
-    __syncthreads();
-  }
+  for (int b = 0; b < HB; ++b) dma_h(b < nk ? b : 0, hsm[b]);
+  __builtin_amdgcn_s_waitcnt(waitcnt_enc(0, 0));
+  __syncthreads();
 
   for (int vt = g; vt < a.n_vtiles; vt += a.P) {
-    const int vbase = vt * kVocabTile + wave * kVocabPerWave;
+    const int vbase = vt * kVocabTile + wv * kVocabPerWave;
+    const __amdgpu_buffer_rsrc_t wr = wres_of(vt);
 
-    f32x16_t acc[kVB][NB];
+    // W ring, first RING chunks of the tile, issued in chunk order (pinned:
+    // vmcnt retires in order, so waits for the first chunks need not drain
+    // the later ones)
+    u32x4_t ring[RING][8];
+#pragma unroll
+    for (int r = 0; r < RING; ++r) {
+      const uint32_t oob = (uint32_t)(r >= nk) << 31;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        __builtin_amdgcn_sched_barrier(0);
+        ring[r][j] = __builtin_amdgcn_raw_buffer_load_b128(
+            wr, ((uint32_t)r * kPackChunkBytes + lane_off + (uint32_t)j * 1024u) | oob, 0, kNonTemporal);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    f32x16_t acc[kVB][NBW];
 #pragma unroll
     for (int vb = 0; vb < kVB; ++vb)
 #pragma unroll
-      for (int pb = 0; pb < NB; ++pb)
+      for (int pb = 0; pb < NBW; ++pb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[vb][pb][i] = 0.f;
 
     // One chunk c (LDS buffer hcur, W registers wreg).  Per MFMA step s the
     // issue order is pinned by scheduling barriers: for each B fragment, its
     // two MFMAs and then the LDS read of the same fragment of step s+1 into
-    // the register just consumed; then the two W loads of chunk c+2 into the
-    // W registers of step s.  Step 3 is split around the chunk's only
+    // the register just consumed; then the two W loads of chunk c+RING into
+    // the W registers of step s.  Step 3 is split around the chunk's only
     // barrier: the first half of its MFMAs, a wait for this wave's DMA of
-    // H(c+1) (vmcnt retires in order; the eight W loads issued after it may
-    // stay in flight) and for its LDS reads, the barrier, then the reads of
-    // step 0 of chunk c+1 and the DMA of H(c+2) into the buffer just
-    // released, then the rest.  The stream runs on into the next tile: W
-    // chunk c+2 past the end is chunk c+2-nk2 of the next tile, and H is the
-    // same for every tile of the workgroup.
-    auto chunk = [&](int c, u32x4_t (&wreg)[8], uint8_t* hcur, uint8_t* hoth) {
-      const int cw = c + 2;
-      const bool to_next = cw >= nk2;
-      const __amdgpu_buffer_rsrc_t wr = to_next ? wnext : wcur;
-      const int cl = to_next ? cw - nk2 : cw;
-      const uint32_t woob = (uint32_t)(cl >= nk) << 31;
-      const uint32_t wbase = (uint32_t)cl * kPackChunkBytes + lane_off;
-      const int hc2 = cl < nk ? cl : 0;   // H chunk c+2 (any valid chunk for a phantom one)
+    // H(c+1) (kDmaLag later loads may stay in flight) and for its LDS reads,
+    // the barrier, then the reads of step 0 of chunk c+1 from hnext and the
+    // DMA of H(c+HB) into hcur (every wave has read its last fragment of
+    // chunk c before the barrier), then the rest.
+    auto chunk = [&](int c, u32x4_t (&wreg)[8], uint8_t* hcur, const uint8_t* hnext) {
+      const uint32_t woob = (uint32_t)(c + RING >= nk) << 31;
+      const uint32_t wbase = (uint32_t)(c + RING) * kPackChunkBytes + lane_off;
+      const int h2 = c + HB < nkr ? c + HB : c + HB - nkr;
+      const int hc2 = h2 < nk ? h2 : 0;   // any valid chunk for a padding one
       auto mfma2 = [&](int s, int pb) {
         const bf16x8_t a0 = as_bf16x8(wreg[2 * s]), a1 = as_bf16x8(wreg[2 * s + 1]);
         acc[0][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfr[pb], acc[0][pb], 0, 0, 0);
@@ -669,7 +683,7 @@ k_project_packed(const ProjArgs a) {
 #pragma unroll
       for (int s = 0; s < 3; ++s) {
 #pragma unroll
-        for (int pb = 0; pb < NB; ++pb) {
+        for (int pb = 0; pb < NBW; ++pb) {
           __builtin_amdgcn_sched_barrier(0);
           mfma2(s, pb);
           __builtin_amdgcn_sched_barrier(0);
@@ -679,56 +693,49 @@ k_project_packed(const ProjArgs a) {
         wload(s);
       }
 #pragma unroll
-      for (int pb = 0; pb < NB / 2; ++pb) {
+      for (int pb = 0; pb < NBW / 2; ++pb) {
         __builtin_amdgcn_sched_barrier(0);
         mfma2(3, pb);
       }
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_enc(8, 0));
+      __builtin_amdgcn_s_waitcnt(waitcnt_enc(kDmaLag, 0));
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int pb = 0; pb < NB / 2; ++pb) bfr[pb] = read_b(hoth, 0, pb);
+      for (int pb = 0; pb < NBW / 2; ++pb) bfr[pb] = read_b(hnext, 0, pb);
       __builtin_amdgcn_sched_barrier(0);
       dma_h(hc2, hcur);
 #pragma unroll
-      for (int pb = NB / 2; pb < NB; ++pb) {
+      for (int pb = NBW / 2; pb < NBW; ++pb) {
         __builtin_amdgcn_sched_barrier(0);
         mfma2(3, pb);
         __builtin_amdgcn_sched_barrier(0);
-        bfr[pb] = read_b(hoth, 0, pb);
+        bfr[pb] = read_b(hnext, 0, pb);
       }
       __builtin_amdgcn_sched_barrier(0);
       wload(3);
       __builtin_amdgcn_sched_barrier(0);
     };
-    // step-0 fragments of chunk 0 (H chunk 0 is in hsm0: loaded in the
-    // prologue or by the previous tile's stream, which waited for it); read
-    // here rather than carried through the epilogue, where registers are short
+    // step-0 fragments of chunk 0 (H chunk 0 is in hsm[0]: loaded in the
+    // prologue or by the previous tile's stream, which waited for it)
 #pragma unroll
-    for (int pb = 0; pb < NB; ++pb) bfr[pb] = read_b(hsm0, 0, pb);
-    for (int c = 0; c < nk2; c += 2) {
-      chunk(c, wx, hsm0, hsm1);
-      chunk(c + 1, wy, hsm1, hsm0);
+    for (int pb = 0; pb < NBW; ++pb) bfr[pb] = read_b(hsm[0], 0, pb);
+    for (int c = 0; c < nkr; c += RING) {
+#pragma unroll
+      for (int r = 0; r < RING; ++r) chunk(c + r, ring[r], hsm[r % HB], hsm[(r + 1) % HB]);
     }
-    wcur = wnext;
-    wnext = wres_of(vt + 2 * a.P);
 
     // ---------------- epilogue: one position per lane per block ----------
+    // One loop body for all blocks (not unrolled: it is long).  Block pb is
+    // always taken from acc[.][0] and the accumulators are rotated down one
+    // block at the end of the body, so every register index stays static and
+    // the accumulators never leave AGPRs.
 #pragma unroll 1
-    for (int pb = 0; pb < NB; ++pb) {
+    for (int pb = 0; pb < NBW; ++pb) {
       f32x16_t z[kVB];
-      switch (pb) {
-#define DGD_TAKE(P)                                            \
-  case P:                                                      \
-    _Pragma("unroll") for (int vb = 0; vb < kVB; ++vb)         \
-        z[vb] = acc[vb][(P) < NB ? (P) : 0];                   \
-    break;
-        DGD_TAKE(0) DGD_TAKE(1) DGD_TAKE(2) DGD_TAKE(3)
-        DGD_TAKE(4) DGD_TAKE(5) DGD_TAKE(6) DGD_TAKE(7)
-#undef DGD_TAKE
-      }
-      const int r = row0 + pb * 32 + col;
+#pragma unroll
+      for (int vb = 0; vb < kVB; ++vb) z[vb] = acc[vb][0];
+      const int r = row0 + wp * PPW + pb * 32 + col;
       const bool rvalid = r < a.M;
       int cv = rvalid ? r / a.L : 0;
       if constexpr (kUniformKey) cv = __builtin_amdgcn_readfirstlane(cv);
@@ -752,18 +759,23 @@ k_project_packed(const ProjArgs a) {
       }
       const Rec wrec = tile_record(z, vbase, half, a.V, a.c2, pabs, (uint32_t)a.gstep, key0, key1);
       if (half == 0) {
-        Rec* slot = recs + wave * MROWS + pb * 32 + col;
+        Rec* slot = recs + wave * PPW + pb * 32 + col;
         rec_store(slot, rec_merge(rec_load(slot), wrec));
       }
+#pragma unroll
+      for (int vb = 0; vb < kVB; ++vb)
+#pragma unroll
+        for (int k = 0; k + 1 < NBW; ++k) acc[vb][k] = acc[vb][k + 1];
     }
   }
 
   // ------- merge the four vocabulary waves of each position (fixed order) -------
   __syncthreads();
-  for (int t = tid; t < MROWS; t += kThreads) {
-    Rec r = rec_load(recs + t);
+  for (int t = tid; t < MROWS; t += THREADS) {
+    const int tp = t / PPW, lp = t % PPW;
+    Rec r = rec_load(recs + (tp * 4) * PPW + lp);
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) r = rec_merge(r, rec_load(recs + w * MROWS + t));
+    for (int w = 1; w < 4; ++w) r = rec_merge(r, rec_load(recs + (tp * 4 + w) * PPW + lp));
     const int row = row0 + t;
     if (row < a.M) rec_store(a.part + (size_t)row * a.P + g, r);
   }
@@ -1192,14 +1204,29 @@ void launch_project_mb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits,
   }
 }
 
+// Launch shape of the packed projection: waves per SIMD, W ring depth and H
+// buffers.
+#ifndef DGD_PACKED_PW
+#define DGD_PACKED_PW 1
+#endif
+#ifndef DGD_PACKED_RING
+#define DGD_PACKED_RING 2
+#endif
+#ifndef DGD_PACKED_HB
+#define DGD_PACKED_HB 2
+#endif
+constexpr int kPackedPW = DGD_PACKED_PW, kPackedRing = DGD_PACKED_RING, kPackedHB = DGD_PACKED_HB;
+
 template <int NB>
 void launch_packed_nb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits, bool uniform) {
+  constexpr int PW = kPackedPW, R = kPackedRing, HB = kPackedHB;
+  const dim3 block(256 * PW);
   if (logits) {
-    if (uniform) hipLaunchKernelGGL((k_project_packed<NB, true, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_project_packed<NB, true, false>), grid, dim3(kThreads), 0, s, a);
+    if (uniform) hipLaunchKernelGGL((k_project_packed<NB, true, true, PW, R, HB>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_project_packed<NB, true, false, PW, R, HB>), grid, block, 0, s, a);
   } else {
-    if (uniform) hipLaunchKernelGGL((k_project_packed<NB, false, true>), grid, dim3(kThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_project_packed<NB, false, false>), grid, dim3(kThreads), 0, s, a);
+    if (uniform) hipLaunchKernelGGL((k_project_packed<NB, false, true, PW, R, HB>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_project_packed<NB, false, false, PW, R, HB>), grid, block, 0, s, a);
   }
 }
 
