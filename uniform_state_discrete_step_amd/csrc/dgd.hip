@@ -162,21 +162,22 @@ constexpr int waitcnt_enc(int vm, int lgkm) {
 // Record of one position over the 64 vocabulary ids held by a lane pair:
 // z[vb][4q + e] (lane half h) is the logit of id vbase + 32 vb + 8 q + 4 h + e.
 // The two halves' records are merged; both lanes return the merged record.
+template <bool kUniformKey>
 __device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int half, int V, float c2,
                                            uint32_t pabs, uint32_t gstep, uint32_t key0,
                                            uint32_t key1) {
-  // Tempered logits in bits: x = z * c2, recomputed in each pass rather
-  // than kept (registers are the scarce resource here).  The multiply is
-  // never fused with the following add, so every pass sees the same x.
-  // value index i = vb*16 + 4q + e  <->  vocabulary id vbase + vb*32 + 8q + 4h + e.
-  // In a ragged last tile, ids past V get the logit kMasked, far below
-  // the running-max start kNeg: they add exact zeros to S and A and never
-  // win the argmax or the sample.
+  // Tempered logits in bits, x2 = z * c2, computed once in place (a plain,
+  // non-contracted multiply).  value index i = vb*16 + 4q + e  <->
+  // vocabulary id vbase + vb*32 + 8q + 4h + e.  In a ragged last tile, ids
+  // past V get kMasked, far below the running-max start kNeg: they add exact
+  // zeros to S and A and never win the argmax or the sample.
+#pragma unroll
+  for (int i = 0; i < kVB * 16; ++i) z[i >> 4][i & 15] = __fmul_rn(z[i >> 4][i & 15], c2);
   if (vbase + kVocabPerWave > V) {
 #pragma unroll
     for (int i = 0; i < kVB * 16; ++i) {
       const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
-      z[i >> 4][i & 15] = v < V ? z[i >> 4][i & 15] : kMasked / c2;
+      z[i >> 4][i & 15] = v < V ? z[i >> 4][i & 15] : kMasked;
     }
   }
   float m = kNeg;
@@ -184,7 +185,7 @@ __device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int ha
 #pragma unroll
   for (int i = 0; i < kVB * 16; ++i) {   // first maximum (ids increase with i)
     const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
-    const float x = __fmul_rn(z[i >> 4][i & 15], c2);
+    const float x = z[i >> 4][i & 15];
     am = x > m ? v : am;
     m = fmaxf(m, x);
   }
@@ -195,7 +196,7 @@ __device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int ha
   float S = 0.f, A = 0.f;
 #pragma unroll
   for (int i = 0; i < kVB * 16; ++i) {
-    const float dx = __fmul_rn(z[i >> 4][i & 15], c2) - m;
+    const float dx = z[i >> 4][i & 15] - m;
     const float e = fexp2(dx);
     S += e;
     A = fmaf(dx, e, A);
@@ -206,12 +207,16 @@ __device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int ha
 #pragma unroll
   for (int grp = 0; grp < kVB * 4; ++grp) {
     const int v0 = vbase + (grp >> 2) * 32 + 8 * (grp & 3) + 4 * half;
-    const Philox4 pw = philox4x32_10((uint32_t)v0 >> 2, pabs, gstep, 0u, key0, key1);
+    Philox4 pw;
+    if constexpr (kUniformKey)
+      pw = philox4x32_10_uniform_key((uint32_t)v0 >> 2, pabs, gstep, 0u, key0, key1);
+    else
+      pw = philox4x32_10((uint32_t)v0 >> 2, pabs, gstep, 0u, key0, key1);
     const uint32_t words[4] = {pw.x, pw.y, pw.z, pw.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {   // top two, first index on ties
       const int i = 4 * grp + e;
-      const float y = __fmul_rn(z[i >> 4][i & 15], c2) + gumbel_bits(words[e]);
+      const float y = z[i >> 4][i & 15] + gumbel_bits(words[e]);
       y2 = fmaxf(y2, fminf(y, y1));
       i1 = y > y1 ? v0 + e : i1;
       y1 = fmaxf(y1, y);
@@ -448,7 +453,7 @@ k_project(const ProjArgs a) {
         }
       }
 
-      const Rec wrec = tile_record(z, vbase, half, a.V, a.c2, pabs, (uint32_t)a.gstep, key0, key1);
+      const Rec wrec = tile_record<kUniformKey>(z, vbase, half, a.V, a.c2, pabs, (uint32_t)a.gstep, key0, key1);
       if (half == 0) {
         Rec* slot = recs + wave * PPW + pb * 32 + col;
         rec_store(slot, rec_merge(rec_load(slot), wrec));
@@ -757,7 +762,7 @@ k_project_packed(const ProjArgs a) {
             }
         }
       }
-      const Rec wrec = tile_record(z, vbase, half, a.V, a.c2, pabs, (uint32_t)a.gstep, key0, key1);
+      const Rec wrec = tile_record<kUniformKey>(z, vbase, half, a.V, a.c2, pabs, (uint32_t)a.gstep, key0, key1);
       if (half == 0) {
         Rec* slot = recs + wave * PPW + pb * 32 + col;
         rec_store(slot, rec_merge(rec_load(slot), wrec));

@@ -55,6 +55,35 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   return {c0, c1, c2, c3};
 }
 
+// The same generator for a wave-uniform key (held in scalar registers): each
+// round's two three-way XORs are single v_bitop3_b32 instructions (truth
+// table 0x96 = a ^ b ^ c) with the round key as the scalar operand.
+__device__ __forceinline__ uint32_t xor3_key(uint32_t a, uint32_t b, uint32_t k) {
+  uint32_t r;
+  asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+  return r;
+}
+
+__device__ __forceinline__ Philox4 philox4x32_10_uniform_key(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                             uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t prod0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t prod1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = xor3_key((uint32_t)(prod1 >> 32), c1, k0);
+    const uint32_t n2 = xor3_key((uint32_t)(prod0 >> 32), c3, k1);
+    c1 = (uint32_t)prod1;
+    c3 = (uint32_t)prod0;
+    c0 = n0;
+    c2 = n2;
+  }
+  return {c0, c1, c2, c3};
+}
+
 // Uniform token in [0, V) from a word: the high half of w * V.
 __device__ __forceinline__ int32_t word_to_token(uint32_t w, uint32_t V) {
   return (int32_t)(((uint64_t)w * V) >> 32);
