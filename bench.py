@@ -35,6 +35,23 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counters
+    (profiles/<kernel>_gemma_vocab_traffic.json), or None when the library
+    sources have changed since those counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"{kernel}_gemma_vocab_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+
+
 def cpu_baseline(wl, W, Hs):
     """Time the oracle (as it stands) on one full step of the workload."""
     from oracle import dgd_oracle as O
@@ -165,8 +182,10 @@ def main():
              "frac": hbm_frac} if bound == "hbm" else
             {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": mfma_frac})
-    roof.update({"traffic": None,
-                 "kernel": "k_project_packed" if layout == dgd.DGD_VOCAB_PACKED else "k_project", "kernel_avg_us": k1_avg_s * 1e6,
+    kname = "k_project_packed" if layout == dgd.DGD_VOCAB_PACKED else "k_project"
+    traffic = measured_traffic(kname) if wl.name == "gemma_vocab" else None
+    roof.update({"traffic": traffic,
+                 "kernel": kname, "kernel_avg_us": k1_avg_s * 1e6,
                  "kernel_launches": k1_n, "algorithmic_bytes_per_launch": alg_bytes,
                  "flops_per_launch": flops,
                  "other": {"hbm_GBs": gbs, "hbm_frac": hbm_frac, "mfma_TFLOPs": tflops,
