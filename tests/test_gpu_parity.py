@@ -87,6 +87,8 @@ def test_tiny_variants(dev, variant, layout):
     dict(V=129, d=8, L=1, B=2, G=3, N=4),          # one-position canvases, 3 blocks
     dict(V=1, d=16, L=5, B=1, G=5, N=3),           # one-token vocabulary
     dict(V=4096, d=136, L=70, B=2, G=70, N=6),     # rows straddle 32-row blocks of one tile
+    dict(V=1024, d=64, L=600, B=1, G=600, N=4),    # canvas over 512: sorting network path
+    dict(V=2048, d=128, L=512, B=2, G=512, N=3),   # largest canvas of the counting-rank path
 ])
 def test_ragged_shapes(dev, shape, layout):
     B = shape["B"]

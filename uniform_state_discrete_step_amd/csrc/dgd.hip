@@ -1,16 +1,17 @@
 // libdgd: the per-step denoising update of uniform-state discrete diffusion
 // on AMD Instinct MI355X (gfx950, CDNA4).
 //
-// Per step, two kernels:
-//   k_project       bf16 MFMA projection z = H W^T (W streamed once from HBM,
+// Per step, three kernels:
+//   k_project_packed (or k_project for a row-major table)
+//                   bf16 MFMA projection z = H W^T (W streamed once from HBM,
 //                   H chunks staged through LDS) fused with the tempered
 //                   softmax-entropy, argmax and Gumbel-max reductions in its
 //                   epilogue; writes one 32-byte partial record per
 //                   (position, vocabulary group).  Logits stay in registers.
-//   k_merge_commit  merges the partial records of each position, then the
-//                   last workgroup of each canvas applies the early-stop
-//                   rule, sorts the open positions by entropy, applies the
-//                   entropy bound, writes samples and re-noises the rest.
+//   k_merge         merges the partial records of each position;
+//   k_commit        one workgroup per canvas applies the early-stop rule,
+//                   sorts the open positions by entropy, applies the entropy
+//                   bound, writes samples and re-noises the rest.
 // plus k_init_block at the start of each block.
 //
 // The method follows "The Annotated DiffusionGemma" walkthrough, section
@@ -64,7 +65,6 @@ struct ProjArgs {
   Rec* part;              // [M][P]
   float* logits;          // [M][V] (validation) or null
   const int32_t* done;    // [B]
-  int32_t* counters;      // [B], zeroed here for the commit kernel
   int32_t M, V, d, L, B;
   int32_t P, n_vtiles, n_mtiles;
   int32_t block, gstep;
@@ -93,7 +93,6 @@ struct CommitArgs {
   int32_t* st_ncomm;
   float* st_mean;
   int32_t* st_new;
-  int32_t* counters;
   int32_t B, L, G, V, N, block, step, gstep, freeze, final_emit, stab;
   float conf;
   float bound[DGD_MAX_CANVASES];
@@ -275,8 +274,6 @@ k_project(const ProjArgs a) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, half = lane >> 5, col = lane & 31;
   const int wv = wave & (kVGroups - 1), wp = wave / kVGroups;
-
-  if (blockIdx.x == 0 && tid < a.B) a.counters[tid] = 0;
 
   int mt, g;
   tile_of_block(blockIdx.x, a.n_mtiles, a.P, mt, g);
@@ -558,8 +555,6 @@ k_project_packed(const ProjArgs a) {
   const int wv = wave & 3, wp = wave >> 2;
   const int lane = tid & 63, half = lane >> 5, col = lane & 31;
 
-  if (blockIdx.x == 0 && tid < a.B) a.counters[tid] = 0;
-
   int mt, g;
   tile_of_block(blockIdx.x, a.n_mtiles, a.P, mt, g);
   const int row0 = mt * MROWS;
@@ -787,63 +782,75 @@ k_project_packed(const ProjArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// k_merge_commit
+// k_merge, k_commit
 // ---------------------------------------------------------------------------
-__device__ inline double block_sum_f64(double v, double* red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
-  __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const double out = red[0];
-  __syncthreads();
-  return out;
-}
-
+// Sum of one int per thread over the workgroup (wave butterflies, then LDS).
 __device__ inline int block_sum_i32(int v, int* red) {
-  const int tid = threadIdx.x;
-  red[tid] = v;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if (lane == 0) red[wave] = v;
   __syncthreads();
-  for (int s = kThreads / 2; s > 0; s >>= 1) {
-    if (tid < s) red[tid] += red[tid + s];
-    __syncthreads();
-  }
-  const int out = red[0];
+  int out = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) out += red[w];
   __syncthreads();
   return out;
 }
 
-// Commit phase of one canvas, run by the whole (last) workgroup.
+// Commit phase of one canvas, run by one workgroup.  The per-position
+// results are read from memory once, into LDS.  The two float64 running sums
+// the rule defines (the mean entropy over positions 0..L-1, and the exclusive
+// prefix over the ranked entropies) are added by one lane in that order, so
+// they are the same doubles however many threads run.
 __device__ void commit_canvas(const CommitArgs& a, int c) {
-  __shared__ unsigned long long keys[DGD_MAX_CANVAS_LEN];
-  __shared__ double dred[kThreads];
-  __shared__ int ired[kThreads];
+  __shared__ unsigned long long keys[DGD_MAX_CANVAS_LEN];    // (entropy bits, position)
+  __shared__ unsigned long long ranked[DGD_MAX_CANVAS_LEN];  // eligible keys in rank order
+  __shared__ double escan[DGD_MAX_CANVAS_LEN];
+  __shared__ float hrow[DGD_MAX_CANVAS_LEN];
+  __shared__ int ired[kWaves];
+  __shared__ double s_mean;
   const int tid = threadIdx.x;
   const int L = a.L;
   const size_t rbase = (size_t)c * L;
   const size_t cbase = (size_t)c * a.G + (size_t)a.block * L;
 
-  // early stop: mean entropy over the block and argmax stability
-  double hsum = 0.0;
-  int moved = 0;
+  int moved = 0, elig = 0;
   for (int p = tid; p < L; p += kThreads) {
-    hsum += (double)a.rowH[rbase + p];
-    moved += (a.rowA[rbase + p] != a.st_prev[rbase + p]);
+    const float h = a.rowH[rbase + p];
+    const int am = a.rowA[rbase + p];
+    hrow[p] = h;
+    moved += (am != a.st_prev[rbase + p]);
+    const bool e = a.freeze == 0 || a.committed[cbase + p] == 0;
+    keys[p] = e ? (((unsigned long long)__float_as_uint(h) << 32) | (unsigned)p) : ~0ull;
+    elig += e;
   }
-  const double mean = block_sum_f64(hsum, dred) / (double)L;
-  const bool stable = block_sum_i32(moved, ired) == 0;
+  __syncthreads();
+  if (tid == 0) {   // mean entropy over the block, positions in order
+    double hs = 0.0;
+    int p = 0;
+    for (; p + 16 <= L; p += 16) {   // 16 values per batch: the LDS reads overlap
+      float h[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) h[j] = hrow[p + j];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) hs += (double)h[j];
+    }
+    for (; p < L; ++p) hs += (double)hrow[p];
+    s_mean = hs / (double)L;
+  }
+  const bool stable = block_sum_i32(moved, ired) == 0;   // (its barriers also publish s_mean)
+  const int n_elig = block_sum_i32(elig, ired);
+  const double mean = s_mean;
   const int sc = stable ? a.st_stable[c] + 1 : 0;
   const bool converged = mean < (double)a.conf && sc >= a.stab;
   const bool final_step = converged || a.step == a.N - 1;
 
-  int new_commits = 0, open_before = 0;
+  int new_commits = 0;
   if (final_step) {
     for (int p = tid; p < L; p += kThreads) {
       const size_t idx = cbase + p;
       const bool open = a.committed[idx] == 0;
-      open_before += open;
       if (a.freeze == 0 || open) {
         a.canvas[idx] = a.final_emit ? a.rowA[rbase + p] : a.rowTok[rbase + p];
         a.committed[idx] = 1;
@@ -858,62 +865,64 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
       a.st_ncomm[c] = L;
     }
   } else {
-    int n2 = 1;
-    while (n2 < L) n2 <<= 1;
-    int elig = 0;
-    for (int i = tid; i < n2; i += kThreads) {
-      unsigned long long k = ~0ull;
-      if (i < L && (a.freeze == 0 || a.committed[cbase + i] == 0)) {
-        k = ((unsigned long long)__float_as_uint(a.rowH[rbase + i]) << 32) | (unsigned)i;
-        ++elig;
+    // rank the eligible keys, ascending (entropy bits order entropies >= 0;
+    // positions break ties; keys are distinct)
+    if (L <= 512) {
+      // rank by counting: every thread compares its keys with all others
+      for (int p = tid; p < L; p += kThreads) {
+        const unsigned long long k = keys[p];
+        if (k == ~0ull) continue;
+        int rank = 0;
+#pragma unroll 16
+        for (int j = 0; j < L; ++j) rank += keys[j] < k;
+        ranked[rank] = k;
       }
-      keys[i] = k;
-    }
-    const int n_elig = block_sum_i32(elig, ired);   // also orders the key writes
-    // bitonic sort, ascending (entropy bits are monotone: entropies are >= 0)
-    for (int k = 2; k <= n2; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < n2; i += kThreads) {
-          const int ixj = i ^ j;
-          if (ixj > i) {
-            const unsigned long long ki = keys[i], kj = keys[ixj];
-            const bool up = (i & k) == 0;
-            if ((ki > kj) == up) { keys[i] = kj; keys[ixj] = ki; }
+    } else {
+      int n2 = 1;
+      while (n2 < L) n2 <<= 1;
+      for (int i = tid; i < n2; i += kThreads) ranked[i] = i < L ? keys[i] : ~0ull;
+      __syncthreads();
+      for (int k = 2; k <= n2; k <<= 1) {   // bitonic sort
+        for (int j = k >> 1; j > 0; j >>= 1) {
+          for (int i = tid; i < n2; i += kThreads) {
+            const int ixj = i ^ j;
+            if (ixj > i) {
+              const unsigned long long ki = ranked[i], kj = ranked[ixj];
+              const bool up = (i & k) == 0;
+              if ((ki > kj) == up) { ranked[i] = kj; ranked[ixj] = ki; }
+            }
           }
+          __syncthreads();
         }
-        __syncthreads();
       }
     }
-    // exclusive float64 running sum over ranks: contiguous chunk per thread
-    const int per = (n2 + kThreads - 1) / kThreads;
-    const int r0 = tid * per;
-    double loc = 0.0;
-    for (int k = 0; k < per; ++k) {
-      const int rk = r0 + k;
-      if (rk < n_elig) loc += (double)__uint_as_float((unsigned)(keys[rk] >> 32));
-    }
-    dred[tid] = loc;
     __syncthreads();
+    // exclusive float64 running sum over the ranks, in rank order
     if (tid == 0) {
       double run = 0.0;
-      for (int t = 0; t < kThreads; ++t) {
-        const double v = dred[t];
-        dred[t] = run;
-        run += v;
+      int r0 = 0;
+      for (; r0 + 16 <= n_elig; r0 += 16) {   // 16 ranks per batch: the LDS reads overlap
+        double h[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) h[j] = (double)__uint_as_float((unsigned)(ranked[r0 + j] >> 32));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          escan[r0 + j] = run;
+          run += h[j];
+        }
+      }
+      for (; r0 < n_elig; ++r0) {
+        escan[r0] = run;
+        run += (double)__uint_as_float((unsigned)(ranked[r0] >> 32));
       }
     }
     __syncthreads();
-    double E = dred[tid];
     const double bound = (double)a.bound[c];
     const uint32_t k0 = a.key[c][0], k1 = a.key[c][1];
-    for (int k = 0; k < per; ++k) {
-      const int rk = r0 + k;
-      if (rk >= n_elig) break;
-      const unsigned long long key = keys[rk];
-      const int p = (int)(key & 0xffffffffu);
-      const float h = __uint_as_float((unsigned)(key >> 32));
+    for (int rk = tid; rk < n_elig; rk += kThreads) {
+      const int p = (int)(ranked[rk] & 0xffffffffu);
       const size_t idx = cbase + p;
-      if (E <= bound) {
+      if (escan[rk] <= bound) {
         a.canvas[idx] = a.rowTok[rbase + p];
         a.committed[idx] = 1;
         if (a.commit_step) a.commit_step[idx] = (int16_t)a.step;
@@ -924,7 +933,6 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
         a.canvas[idx] = word_to_token(w.x, (uint32_t)a.V);
         a.committed[idx] = 0;
       }
-      E += (double)h;
     }
     new_commits = block_sum_i32(new_commits, ired);
     if (tid == 0) {
@@ -932,7 +940,6 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
       a.st_ncomm[c] = (a.freeze ? (L - n_elig) : 0) + new_commits;
     }
   }
-  (void)open_before;
   if (tid == 0) {
     a.st_stable[c] = sc;
     a.st_steps[c] = a.step + 1;
@@ -944,45 +951,44 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
 }
 
 // Grid (ceil(L/4), B); one wave per position merges that position's partial
-// records; the last workgroup of each canvas commits it.
-__global__ void __launch_bounds__(kThreads) k_merge_commit(const CommitArgs a) {
+// records (fixed order: lanes over the groups, then a butterfly).
+__global__ void __launch_bounds__(kThreads) k_merge(const CommitArgs a) {
   const int c = blockIdx.y;
   if (a.st_done[c]) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int p = blockIdx.x * kWaves + wave;
-  if (p < a.L) {
-    const size_t r = (size_t)c * a.L + p;
-    const Rec* pr = a.part + r * a.P;
-    Rec rec = rec_empty();
-    for (int i = lane; i < a.P; i += 64) rec = rec_merge(rec, rec_load(pr + i));
+  if (p >= a.L) return;
+  const size_t r = (size_t)c * a.L + p;
+  const Rec* pr = a.part + r * a.P;
+  Rec rec = rec_empty();
+  for (int i = lane; i < a.P; i += 64) rec = rec_merge(rec, rec_load(pr + i));
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      const Rec o = rec_shfl_xor(rec, off);
-      const bool upper = (lane & off) != 0;
-      rec = rec_merge(rec_pick(upper, o, rec), rec_pick(upper, rec, o));
-    }
-    if (lane == 0) {
-      const double S = (double)rec.S, A = (double)rec.A;
-      double Hn = kLn2 * (log2(S) - A / S);
-      if (!(Hn > 0.0)) Hn = 0.0;
-      const float H = (float)Hn;
-      const float gap = (float)(((double)rec.y1 - (double)rec.y2) * kLn2);
-      a.rowH[r] = H;
-      a.rowA[r] = rec.am;
-      a.rowTok[r] = rec.i1;
-      if (a.out_entropy) a.out_entropy[r] = H;
-      if (a.out_argmax) a.out_argmax[r] = rec.am;
-      if (a.out_token) a.out_token[r] = rec.i1;
-      if (a.out_gap) a.out_gap[r] = gap;
-    }
+  for (int off = 32; off > 0; off >>= 1) {
+    const Rec o = rec_shfl_xor(rec, off);
+    const bool upper = (lane & off) != 0;
+    rec = rec_merge(rec_pick(upper, o, rec), rec_pick(upper, rec, o));
   }
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = (atomicAdd(&a.counters[c], 1) == (int)gridDim.x - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+  if (lane == 0) {
+    const double S = (double)rec.S, A = (double)rec.A;
+    double Hn = kLn2 * (log2(S) - A / S);
+    if (!(Hn > 0.0)) Hn = 0.0;
+    const float H = (float)Hn;
+    const float gap = (float)(((double)rec.y1 - (double)rec.y2) * kLn2);
+    a.rowH[r] = H;
+    a.rowA[r] = rec.am;
+    a.rowTok[r] = rec.i1;
+    if (a.out_entropy) a.out_entropy[r] = H;
+    if (a.out_argmax) a.out_argmax[r] = rec.am;
+    if (a.out_token) a.out_token[r] = rec.i1;
+    if (a.out_gap) a.out_gap[r] = gap;
+  }
+}
+
+// Grid (B): the commit of every canvas that is not done, one workgroup each
+// (the kernel boundary after k_merge publishes the per-position results).
+__global__ void __launch_bounds__(kThreads) k_commit(const CommitArgs a) {
+  const int c = blockIdx.x;
+  if (a.st_done[c]) return;
   commit_canvas(a, c);
 }
 
@@ -1036,7 +1042,7 @@ int hip_fail(hipError_t e, const char* what) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t part, rowH, rowA, rowTok, counters, total;
+  size_t part, rowH, rowA, rowTok, total;
   int P;
 };
 
@@ -1049,7 +1055,6 @@ WsLayout ws_layout(int B, int L, int V) {
   w.rowH = off;     off = align256(off + M * sizeof(float));
   w.rowA = off;     off = align256(off + M * sizeof(int32_t));
   w.rowTok = off;   off = align256(off + M * sizeof(int32_t));
-  w.counters = off; off = align256(off + (size_t)B * sizeof(int32_t));
   w.total = off;
   return w;
 }
@@ -1253,7 +1258,6 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   pa.part = (Rec*)(ws + wl.part);
   pa.logits = ctx->logits;
   pa.done = sv.done;
-  pa.counters = (int32_t*)(ws + wl.counters);
   pa.M = M; pa.V = V; pa.d = dd; pa.L = L; pa.B = B;
   pa.P = wl.P;
   pa.n_vtiles = num_vtiles(V);
@@ -1301,7 +1305,6 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   ca.canvas = canvas; ca.committed = committed;
   ca.st_prev = sv.prev; ca.st_stable = sv.stable; ca.st_done = sv.done; ca.st_steps = sv.steps;
   ca.st_conv = sv.conv; ca.st_ncomm = sv.ncomm; ca.st_mean = sv.mean; ca.st_new = sv.newc;
-  ca.counters = pa.counters;
   ca.B = B; ca.L = L; ca.G = ctx->G; ca.V = V; ca.N = N;
   ca.block = block; ca.step = step; ca.gstep = gstep;
   ca.freeze = prm->freeze; ca.final_emit = prm->final_emit; ca.stab = prm->stability_threshold;
@@ -1309,9 +1312,12 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   for (int c = 0; c < B; ++c) ca.bound[c] = ctx->entropy_bound[c];
   fill_keys(ca.key, seed, B);
   const dim3 grid2((L + kWaves - 1) / kWaves, B);
-  hipLaunchKernelGGL(k_merge_commit, grid2, dim3(kThreads), 0, stream, ca);
+  hipLaunchKernelGGL(k_merge, grid2, dim3(kThreads), 0, stream, ca);
   e = hipGetLastError();
-  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_merge_commit launch");
+  if (e != hipSuccess) return hip_fail(e, "k_merge launch");
+  hipLaunchKernelGGL(k_commit, dim3(B), dim3(kThreads), 0, stream, ca);
+  e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_commit launch");
 }
 
 }  // namespace
