@@ -52,6 +52,14 @@ pages this work follows; citations give page and section):
 
 All functions below are deliberately direct: one pass per definition, no
 blocking, fusion or streaming.  Every function is pinned by the CPU tests.
+
+Parity unpinned: three readings cannot be pinned to the pages because the
+pages disagree; the tests pin the oracle to the readings, not the readings to
+the pages.  They are the sticky freeze of committed positions (point 7; the
+walkthrough's loop re-ranks every position), what `confidence` measures
+(point 6; the node page calls it a probability, the TensorSharp doc a mean
+entropy), and the end of a block (point 6; the walkthrough returns a sample on
+convergence and has no exit after N steps).
 """
 from __future__ import annotations
 
