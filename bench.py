@@ -70,10 +70,19 @@ def cpu_baseline(wl, W, Hs):
         for s in range(steps):
             st, _ = O.step(st, Hs[0, s, c], W, 0, s, P, wl.seeds[c], wl.bounds[c])
     dt = time.perf_counter() - t0
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     return {
         "value": steps / dt,
         "unit": "steps/s",
         "cores": int(cores),
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"{steps} denoising step(s) of {wl.name} ({wl.B}x{wl.L} positions x V={wl.V}, "
                   f"d={wl.d}); oracle float64 numpy, projection via BLAS",
@@ -150,16 +159,22 @@ def main():
     log(f"[bench] warmup {args.warmup} steps")
     run_steps(args.warmup)
     torch.cuda.synchronize()
-    start_ev = torch.cuda.Event(enable_timing=True)
-    stop_ev = torch.cuda.Event(enable_timing=True)
+    # the library enqueues on torch's current stream, where the events are
+    # recorded; the K timed steps are split into 5 segments for a spread
+    n_seg = 5 if args.steps >= 5 else 1
+    bounds = [args.steps * i // n_seg for i in range(n_seg + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n_seg + 1)]
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    start_ev.record()
-    run_steps(args.steps, start=args.warmup)
-    stop_ev.record()
+    evs[0].record()
+    for i in range(n_seg):
+        run_steps(bounds[i + 1] - bounds[i], start=args.warmup + bounds[i])
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
-    ms = start_ev.elapsed_time(stop_ev)
+    ms = evs[0].elapsed_time(evs[-1])
+    seg_ms_per_step = sorted(evs[i].elapsed_time(evs[i + 1]) / (bounds[i + 1] - bounds[i])
+                             for i in range(n_seg))
     log(f"[bench] timed {args.steps} steps: {ms:.2f} ms (wall {wall * 1e3:.2f} ms)")
     if args.profile_only:
         return
@@ -209,6 +224,8 @@ def main():
                    "hidden": wl.d, "gen_length": wl.G, "num_inference_steps": wl.N,
                    "vocab_layout": args.layout},
         "logit_elems_per_s": steps_per_s * M * wl.V,
+        "ms_per_step_segments": {"n": n_seg, "median": seg_ms_per_step[n_seg // 2],
+                                 "min": seg_ms_per_step[0], "max": seg_ms_per_step[-1]},
         "step_frac_of_hbm_floor": (steps_per_s * alg_bytes) / (HBM_PEAK_GBS * 1e9),
         "roofline": roof,
     }

@@ -174,12 +174,16 @@ def test_dgd_run_matches_stepping_and_is_deterministic(dev):
     rep = run.run(sample_every=1000, rows_per_canvas=1)
     _check(rep, wl.name + " stepped")
     outs = []
-    for _ in range(2):
+    # twice with per-step outputs, once without (the benchmark's configuration)
+    quiet = run.dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev, outputs=False,
+                            vocab_layout=1)
+    for ctx in (run.ctx, run.ctx, quiet):
         can = torch.zeros_like(run.canvas)
         com = torch.zeros_like(run.committed)
-        run.dgd.dgd_run(run.Hd.reshape(-1), run.Wd, can, com, run.params, wl.seeds, run.ctx)
+        run.dgd.dgd_run(run.Hd.reshape(-1), run.Wd, can, com, run.params, wl.seeds, ctx)
         torch.cuda.synchronize()
         outs.append((can.cpu().numpy(), com.cpu().numpy()))
+    assert np.array_equal(outs[2][0], outs[0][0]) and np.array_equal(outs[2][1], outs[0][1])
     assert np.array_equal(outs[0][0], outs[1][0]) and np.array_equal(outs[0][1], outs[1][1])
     assert np.array_equal(outs[0][0], run.canvas.cpu().numpy())
     assert np.array_equal(outs[0][1], run.committed.cpu().numpy())

@@ -191,3 +191,51 @@ def test_pack_vocab_layout(dev, V, d):
     expect = Wpad[64 * rg + 32 * f + l % 32, 64 * c + 32 * (l // 32) + 8 * s + j]
     assert got.shape[0] == dgd.dgd_packed_vocab_bytes(V, d) // 2 == expect.size
     assert np.array_equal(got, expect.reshape(-1))
+
+
+# ----------------------------------------------------------------------------
+def test_resume_from_saved_state(dev, layout):
+    """Stopping after a step, saving canvas, mask and state to the host and
+    resuming in a fresh context gives the uninterrupted run, bit for bit."""
+    import torch
+    from uniform_state_discrete_step_amd import dgd
+    wl = shrink(WORKLOADS["tiny"], B=2, G=48, L=16, N=6, seeds=(4, 9), bounds=(0.1, 0.3))
+    W, Hs = make_workload_arrays(wl, threads=1)
+    Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+    if layout == dgd.DGD_VOCAB_PACKED:
+        Wd = dgd.pack_vocab(Wd, wl.V, wl.d)
+    Hd = torch.from_numpy(Hs.view(np.int16)).to(dev)
+    prm = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence, wl.stability_threshold,
+                          wl.freeze, wl.final_emit)
+
+    def ctx():
+        return dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev, vocab_layout=layout)
+
+    def fresh():
+        return (torch.zeros(wl.B * wl.G, dtype=torch.int32, device=dev),
+                torch.zeros(wl.B * wl.G, dtype=torch.uint8, device=dev))
+
+    can_a, com_a = fresh()
+    dgd.dgd_run(Hd.reshape(-1), Wd, can_a, com_a, prm, wl.seeds, ctx())
+    torch.cuda.synchronize()
+
+    def steps(c, can, com, todo):
+        for b, s in todo:
+            if s == 0:
+                dgd.dgd_init_block(can, com, b, prm, wl.seeds, c)
+            dgd.dgd_step(Hd[b, s].reshape(-1), Wd, can, com, b, s, prm, wl.seeds, c)
+
+    order = [(b, s) for b in range(wl.blocks) for s in range(wl.N)]
+    cut = wl.N + 2                      # inside the second block
+    c1 = ctx()
+    can_b, com_b = fresh()
+    steps(c1, can_b, com_b, order[:cut])
+    torch.cuda.synchronize()
+    saved = (can_b.cpu(), com_b.cpu(), c1.state.cpu())
+    c2 = ctx()
+    can_c, com_c = fresh()
+    can_c.copy_(saved[0]); com_c.copy_(saved[1]); c2.state.copy_(saved[2])
+    steps(c2, can_c, com_c, order[cut:])
+    torch.cuda.synchronize()
+    assert np.array_equal(can_c.cpu().numpy(), can_a.cpu().numpy())
+    assert np.array_equal(com_c.cpu().numpy(), com_a.cpu().numpy())
