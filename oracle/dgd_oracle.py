@@ -16,6 +16,10 @@ pages this work follows; citations give page and section):
 2. Logits.  z = H W_vocab^T with the tied embedding table as unembedding
    (walkthrough, "Complete DiffusionGemma model"; TensorSharp doc, "2. Forward
    graph": tied lm-head).  Computed here in float64 from the bf16 inputs.
+   Optionally the model's tail around it: the output RMSNorm
+   h = w x sqrt(d) / (||x|| + eps), rounded to bfloat16, before the
+   projection, and the softcap c tanh(z / c) after it (walkthrough, "RMSNorm"
+   and "Logit Softcapping").
 3. Entropy in nats, H(p) = -sum_v p_v log p_v (walkthrough, "Compute entropy";
    node page, entropy_bound row: natural-log entropy).  float64, then rounded
    to float32: that float32 value is the position's entropy in every later
@@ -117,6 +121,46 @@ def projection(H_bits: np.ndarray, W_bits: np.ndarray, v_chunk: int = 16384,
         Wc = W64[v0:v1] if W64 is not None else bf16_to_f64(W_bits[v0:v1])
         z[:, v0:v1] = H @ Wc.T
     return z
+
+
+# ----------------------------------------------------------------------------
+# 2b. the lm-head tail: output norm before the projection, logit softcap after
+#     (walkthrough, "RMSNorm", "Logit Softcapping" and the end of the model's
+#     forward: rms(x, model_norm), then x @ W_embed^T, then the tanh cap;
+#     TensorSharp doc, "2. Forward graph": output norm -> tied lm-head ->
+#     final logit softcap)
+# ----------------------------------------------------------------------------
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 -> bfloat16 bit patterns, rounded once to nearest, ties to even.
+
+    Each value is rounded at the spacing of bfloat16 in its binade (8
+    significant bits; the subnormal spacing 2^-133 below 2^-126): dividing by
+    a power of two is exact and numpy's rint rounds half to even.  Finite
+    inputs inside the bfloat16 range only.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    _, E = np.frexp(x)                                  # |x| = f 2^E, f in [0.5, 1)
+    e = np.maximum(E - 1, -126)                         # exponent of the binade
+    spacing = np.ldexp(1.0, e - 7)
+    q = np.rint(x / spacing) * spacing                  # exactly a bfloat16 value
+    return (q.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def rms_norm(H_bits: np.ndarray, w_bits: np.ndarray, eps: float) -> np.ndarray:
+    """h = w * x * sqrt(d) / (||x||_2 + eps) per row, in float64, rounded to
+    bfloat16 (the model casts the normalized state back to its dtype before
+    the projection).  H_bits [rows, d], w_bits [d]: bf16 bits."""
+    x = bf16_to_f64(H_bits)
+    w = bf16_to_f64(w_bits)
+    d = x.shape[-1]
+    norm = np.sqrt((x * x).sum(axis=-1, keepdims=True))
+    return round_bf16(w * x * np.sqrt(float(d)) / (norm + float(eps)))
+
+
+def softcap(z: np.ndarray, c: float) -> np.ndarray:
+    """c * tanh(z / c); c = 0 means no cap."""
+    z = np.asarray(z, dtype=np.float64)
+    return z if c == 0 else float(c) * np.tanh(z / float(c))
 
 
 # ----------------------------------------------------------------------------
@@ -361,15 +405,34 @@ def step_from_stats(state: CanvasState, stats: dict, block: int, step: int, L: i
     return s, info
 
 
+@dataclasses.dataclass
+class Tail:
+    """The optional lm-head tail: output-norm weights (bf16 bits [d], None =
+    no norm), its epsilon, and the softcap c (0 = no cap)."""
+    norm_weight: np.ndarray = None
+    norm_eps: float = 0.0
+    softcap: float = 0.0
+
+
+def logits(H_bits: np.ndarray, W_bits: np.ndarray, tail: Tail = None, W64=None) -> np.ndarray:
+    """The step's logits: [output norm ->] projection [-> softcap]."""
+    if tail is not None and tail.norm_weight is not None:
+        H_bits = rms_norm(H_bits, tail.norm_weight, tail.norm_eps)
+    z = projection(H_bits, W_bits, W64=W64)
+    if tail is not None and tail.softcap:
+        z = softcap(z, tail.softcap)
+    return z
+
+
 def step(state: CanvasState, H_bits: np.ndarray, W_bits: np.ndarray, block: int, step_idx: int,
-         params: Params, seed: int, bound: float, W64: np.ndarray = None):
+         params: Params, seed: int, bound: float, W64: np.ndarray = None, tail: Tail = None):
     """One denoising step of one canvas: H_bits [L, d] bf16 bits, W_bits [V, d]."""
     L = H_bits.shape[0]
     V = W_bits.shape[0]
     if state.done:
         return state.copy(), {"skipped": True}
     T = temperature(step_idx, params.N, params.t_min, params.t_max)
-    z = projection(H_bits, W_bits, W64=W64)
+    z = logits(H_bits, W_bits, tail, W64=W64)
     stats = position_stats(z, T, seed, block * L + np.arange(L), block * params.N + step_idx)
     new, info = step_from_stats(state, stats, block, step_idx, L, V, params, seed, bound)
     info["T"] = T
@@ -377,7 +440,7 @@ def step(state: CanvasState, H_bits: np.ndarray, W_bits: np.ndarray, block: int,
 
 
 def run(H_steps: np.ndarray, W_bits: np.ndarray, G: int, params: Params, seeds, bounds,
-        on_step=None):
+        on_step=None, tail: Tail = None):
     """Whole generation for every canvas.  H_steps: [G/L, N, B, L, d] bf16 bits."""
     n_blocks, N, B, L, _ = H_steps.shape
     V = W_bits.shape[0]
@@ -390,7 +453,7 @@ def run(H_steps: np.ndarray, W_bits: np.ndarray, G: int, params: Params, seeds, 
             for c in range(B):
                 before = states[c]
                 states[c], info = step(before, H_steps[b, s_idx, c], W_bits, b, s_idx, params,
-                                       seeds[c], bounds[c])
+                                       seeds[c], bounds[c], tail=tail)
                 if on_step is not None:
                     on_step(b, s_idx, c, before, states[c], info)
             if all(st.done for st in states):

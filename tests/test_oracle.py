@@ -181,6 +181,126 @@ def test_projection_chunking_is_invisible():
 
 
 # ----------------------------------------------------------------------------
+# the lm-head tail: bfloat16 rounding, output RMSNorm, softcap
+# ----------------------------------------------------------------------------
+def test_round_bf16_agrees_with_the_float32_rounding():
+    rng = np.random.default_rng(11)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-30, 30, 4000),
+                        np.ldexp(rng.integers(1, 1 << 24, 200).astype(np.float64), -149)])
+    x32 = x.astype(np.float32)                      # values that float32 holds exactly
+    assert np.array_equal(O.round_bf16(x32.astype(np.float64)), f32_to_bf16_bits(x32))
+
+
+def test_round_bf16_ties_to_even_and_rounds_once():
+    one = 0x3F80
+    assert O.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == one           # tie -> even (down)
+    assert O.round_bf16(np.array([1.0 + 3 * 2.0 ** -8]))[0] == one + 2   # tie -> even (up)
+    assert O.round_bf16(np.array([-(1.0 + 2.0 ** -8)]))[0] == 0x8000 | one
+    # just above the tie: one rounding from float64 goes up; a detour through
+    # float32 would land on the tie and then go down to even
+    assert O.round_bf16(np.array([1.0 + 2.0 ** -8 + 2.0 ** -40]))[0] == one + 1
+    assert O.round_bf16(np.array([2.0 ** -130, 0.0]))[1] == 0
+    assert O.round_bf16(np.array([2.0 ** -130]))[0] == 1 << 3               # subnormal
+
+
+def _norm_inputs(seed, rows=6, d=96):
+    rng = np.random.default_rng(seed)
+    H = bf16(rng.standard_normal((rows, d)) * 3.0)
+    w = bf16(np.exp(rng.uniform(np.log(0.5), np.log(8.0), d)))
+    return H, w
+
+
+def bf16_f64(b):
+    return O.bf16_to_f64(b)
+
+
+def test_rms_norm_hand_example():
+    # x = (3, 4): ||x|| = 5, sqrt(d) = sqrt(2); unit weights
+    out = bf16_f64(O.rms_norm(bf16([[3.0, 4.0]]), bf16([1.0, 1.0]), 0.0))[0]
+    assert np.allclose(out, [0.6 * math.sqrt(2), 0.8 * math.sqrt(2)], rtol=2 ** -8)
+    # twice the weights: twice the output, bit for bit
+    out2 = bf16_f64(O.rms_norm(bf16([[3.0, 4.0]]), bf16([2.0, 2.0]), 0.0))[0]
+    assert np.array_equal(out2, 2 * out)
+
+
+def test_rms_norm_gives_unit_rms_along_the_row():
+    H, _ = _norm_inputs(1)
+    d = H.shape[1]
+    out = bf16_f64(O.rms_norm(H, bf16(np.ones(d)), 0.0))
+    assert np.allclose(np.sqrt((out ** 2).mean(axis=1)), 1.0, rtol=2 ** -8)
+    x = bf16_f64(H)
+    assert np.allclose(out * np.linalg.norm(x, axis=1, keepdims=True) / math.sqrt(d), x,
+                       rtol=2 ** -8, atol=0)       # same direction as the input
+
+
+def test_rms_norm_scale_and_sign_invariance():
+    H, w = _norm_inputs(2)
+    base = O.rms_norm(H, w, 0.0)
+    for k in (-6, -1, 3, 9):                        # powers of two scale exactly
+        Hs = bf16(bf16_f64(H) * 2.0 ** k)
+        assert np.array_equal(O.rms_norm(Hs, w, 0.0), base)
+    assert np.array_equal(O.rms_norm(H ^ np.uint16(0x8000), w, 0.0), base ^ np.uint16(0x8000))
+
+
+def test_rms_norm_epsilon_is_added_to_the_norm():
+    H, w = _norm_inputs(3, rows=4)
+    x = bf16_f64(H)
+    n = np.linalg.norm(x, axis=1)
+    for r in range(H.shape[0]):
+        # eps equal to the row's norm halves the output exactly
+        half = bf16_f64(O.rms_norm(H[r:r + 1], w, float(n[r])))
+        full = bf16_f64(O.rms_norm(H[r:r + 1], w, 0.0))
+        assert np.array_equal(half, full / 2)
+    # a zero row with eps > 0 stays zero
+    assert not bf16_f64(O.rms_norm(bf16(np.zeros((1, 8))), bf16(np.ones(8)), 1e-6)).any()
+
+
+def test_softcap_closed_forms():
+    c = 30.0
+    z = np.linspace(-500, 500, 2001)
+    y = O.softcap(z, c)
+    assert np.all(np.abs(y) < c) and np.all(np.diff(y) > 0)
+    assert np.array_equal(O.softcap(-z, c), -y)
+    assert abs(O.softcap(np.array([c * math.atanh(0.5)]), c)[0] - c / 2) < 1e-12
+    small = np.array([1e-3, -2e-3])
+    assert np.allclose(O.softcap(small, c), small - small ** 3 / (3 * c * c), rtol=1e-15)
+    assert np.array_equal(O.softcap(z, 0.0), z)
+
+
+def test_tail_logits_are_invariant_to_the_hidden_scale():
+    rng = np.random.default_rng(5)
+    H, w = _norm_inputs(4, rows=3, d=64)
+    W = bf16(rng.standard_normal((40, 64)))
+    tail = O.Tail(norm_weight=w, norm_eps=0.0, softcap=15.0)
+    z = O.logits(H, W, tail)
+    assert np.array_equal(O.logits(bf16(bf16_f64(H) * 16.0), W, tail), z)
+    assert np.all(np.abs(z) < 15.0)
+    plain = O.logits(H, W, None)
+    assert np.array_equal(plain, O.projection(H, W))
+    # a cap far above every logit pulls it in by z^3 / (3 c^2) to leading order
+    c = 1e6
+    big = O.logits(H, W, O.Tail(softcap=c))
+    lead = plain ** 3 / (3 * c * c)
+    assert np.all(np.abs((plain - big) - lead) <= 1e-3 * np.abs(lead) + 1e-12 * np.abs(plain))
+
+
+def test_step_with_softcap_keeps_the_argmax():
+    rng = np.random.default_rng(6)
+    L, V, d = 8, 48, 32
+    H = bf16(rng.standard_normal((L, d)))
+    W = bf16(rng.standard_normal((V, d)))
+    P = O.Params(N=4, t_min=0.4, t_max=0.8)
+    st0 = O.init_block(O.new_state(L, L), 0, L, V, 7)
+    _, a = O.step(st0, H, W, 0, 1, P, 7, 0.5)
+    _, b = O.step(st0, H, W, 0, 1, P, 7, 0.5, tail=O.Tail(softcap=2.0))
+    sa, sb = a["stats"], b["stats"]
+    assert np.array_equal(sa["argmax"], sb["argmax"])          # the cap is monotone
+    # a cap of 2 squeezes these logits into (-2, 2): every row is flatter
+    assert np.all(sb["entropy64"] >= sa["entropy64"] - 1e-12)
+    assert np.any(sb["entropy64"] > sa["entropy64"] + 1e-3)
+
+
+# ----------------------------------------------------------------------------
 # entropy and argmax
 # ----------------------------------------------------------------------------
 def test_entropy_of_uniform_row_is_log_v(golden_dir):
