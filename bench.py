@@ -6,7 +6,10 @@ re-noise) over one batch of canvases.  Inputs are seeded synthetic tensors
 resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma_vocab]
-                    [--no-cpu-baseline] [--profile-only]
+                    [--no-cpu-baseline] [--profile-only] [--lm-head-tail]
+
+``--lm-head-tail`` adds the model's output norm before the projection and the
+logit softcap (c = 30) after it.
 
 Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the fused
 projection), timed with HIP events on the library's stream in a separate
@@ -52,7 +55,7 @@ def measured_traffic(kernel):
     return rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
 
 
-def cpu_baseline(wl, W, Hs):
+def cpu_baseline(wl, W, Hs, tail=None):
     """Time the oracle (as it stands) on one full step of the workload."""
     from oracle import dgd_oracle as O
     try:
@@ -68,7 +71,8 @@ def cpu_baseline(wl, W, Hs):
     for c in range(wl.B):
         st = O.init_block(O.new_state(wl.G, wl.L), 0, wl.L, wl.V, wl.seeds[c])
         for s in range(steps):
-            st, _ = O.step(st, Hs[0, s, c], W, 0, s, P, wl.seeds[c], wl.bounds[c])
+            st, _ = O.step(st, Hs[0, s, c], W, 0, s, P, wl.seeds[c], wl.bounds[c],
+                           tail=None if tail is None else O.Tail(**tail))
     dt = time.perf_counter() - t0
     cpu_model = ""
     try:
@@ -98,6 +102,9 @@ def main():
     ap.add_argument("--workload", default="gemma_vocab")
     ap.add_argument("--layout", choices=["packed", "rows"], default="packed",
                     help="vocabulary table layout: packed once before timing (default) or row-major")
+    ap.add_argument("--lm-head-tail", action="store_true",
+                    help="output RMSNorm (eps 1e-6) before the projection and a logit softcap "
+                         "(c = 30) after it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed loop (for rocprofv3 runs)")
@@ -113,7 +120,8 @@ def main():
     import torch
 
     from uniform_state_discrete_step_amd import dgd
-    from uniform_state_discrete_step_amd.inputs import WORKLOADS, make_workload_arrays
+    from uniform_state_discrete_step_amd.inputs import (WORKLOADS, make_norm_weight,
+                                                        make_workload_arrays)
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -127,8 +135,14 @@ def main():
         Wd = dgd.pack_vocab(Wd, wl.V, wl.d)
         torch.cuda.synchronize()
     Hd = torch.from_numpy(Hs.view(np.int16)).to(dev)
+    tail, tkw = None, {}
+    if args.lm_head_tail:
+        tail = {"norm_weight": make_norm_weight(wl.d, wl.cfg_seed), "norm_eps": 1e-6,
+                "softcap": 30.0}
+        tkw = {"norm_weight": torch.from_numpy(tail["norm_weight"].view(np.int16)).to(dev),
+               "norm_eps": tail["norm_eps"], "softcap": tail["softcap"]}
     ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev, outputs=False,
-                      vocab_layout=layout)
+                      vocab_layout=layout, **tkw)
     params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence, wl.stability_threshold,
                              wl.freeze, wl.final_emit)
     canvas = torch.zeros(wl.B * wl.G, dtype=torch.int32, device=dev)
@@ -198,7 +212,8 @@ def main():
             {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": mfma_frac})
     kname = "k_project_packed" if layout == dgd.DGD_VOCAB_PACKED else "k_project"
-    traffic = measured_traffic(kname) if wl.name == "gemma_vocab" else None
+    traffic = (measured_traffic(kname) if wl.name == "gemma_vocab" and not args.lm_head_tail
+               else None)
     roof.update({"traffic": traffic,
                  "kernel": kname, "kernel_avg_us": k1_avg_s * 1e6,
                  "kernel_launches": k1_n, "algorithmic_bytes_per_launch": alg_bytes,
@@ -222,7 +237,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "canvases": wl.B, "canvas_len": wl.L, "vocab": wl.V,
                    "hidden": wl.d, "gen_length": wl.G, "num_inference_steps": wl.N,
-                   "vocab_layout": args.layout},
+                   "vocab_layout": args.layout,
+                   "lm_head_tail": ({"norm_eps": 1e-6, "softcap": 30.0} if args.lm_head_tail
+                                    else None)},
         "logit_elems_per_s": steps_per_s * M * wl.V,
         "ms_per_step_segments": {"n": n_seg, "median": seg_ms_per_step[n_seg // 2],
                                  "min": seg_ms_per_step[0], "max": seg_ms_per_step[-1]},
@@ -231,7 +248,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on one step")
-        out["cpu_baseline"] = cpu_baseline(wl, W, Hs)
+        out["cpu_baseline"] = cpu_baseline(wl, W, Hs, tail)
     print(json.dumps(out), flush=True)
 
 

@@ -128,6 +128,22 @@ typedef struct dgd_params {
  *                  DGD_VOCAB_PACKED (1) when it is the output of dgd_pack_vocab()
  *                  for the same V and d (the faster path: every load of the
  *                  projection is a contiguous 1 KB MFMA fragment)
+ * Optional lm-head tail (walkthrough, "RMSNorm" and "Logit Softcapping";
+ * TensorSharp doc, "2. Forward graph": output norm -> tied lm-head -> final
+ * logit softcap).  Zero-initialised fields leave both off, and H is then
+ * taken as already normalised.
+ *   norm_weight  device bf16[d], 16-byte aligned, or NULL (no output norm).
+ *                When set, each row x of H becomes
+ *                  h = w * x * sqrt(d) / (||x||_2 + norm_eps)
+ *                computed in fp64 and rounded once to bf16 (nearest, ties to
+ *                even); the projection then uses h.
+ *   norm_eps     added to the row's L2 norm (not to its mean square);
+ *                finite, in [0, 1]
+ *   norm_h       device bf16[B*L*d], 16-byte aligned, written with h each
+ *                step; required when norm_weight is set, must not overlap H
+ *   softcap      c: the logits become c * tanh(z / c) before the
+ *                temperature; 0 = no cap, else in [0.01, 10000]
+ * ctx->logits stays the projection z itself, before cap and temperature.
  * Optional host outputs (timing): when k1_ms is not NULL the call records HIP
  * events around every launch of the fused projection kernel, synchronises
  * before returning, and writes the summed kernel time in ms to *k1_ms and the
@@ -148,6 +164,10 @@ typedef struct dgd_ctx {
   double*  k1_ms;
   int32_t* k1_launches;
   int32_t  vocab_layout;   /* DGD_VOCAB_ROWS or DGD_VOCAB_PACKED: how W_vocab is laid out */
+  const dgd_bf16* norm_weight;  /* output-norm weights or NULL */
+  float    norm_eps;
+  float    softcap;
+  dgd_bf16* norm_h;             /* normalised H (scratch the caller owns) */
 } dgd_ctx;
 
 /* State layout (device, int32/float words, in this order):

@@ -47,6 +47,8 @@ class Report:
     conv_band: int = 0
     renoised: int = 0
     accepted: int = 0
+    norm_rows: int = 0
+    norm_inexact: int = 0
     failures: list = dataclasses.field(default_factory=list)
 
     def fail(self, msg):
@@ -57,7 +59,17 @@ class Report:
         return (f"steps={self.steps} positions={self.positions} max|dH|={self.max_entropy_err:.2e} "
                 f"bands: argmax={self.argmax_band} sample={self.sample_band} "
                 f"commit={self.commit_band} convergence={self.conv_band} "
-                f"accepted={self.accepted} renoised={self.renoised}")
+                f"accepted={self.accepted} renoised={self.renoised}"
+                + (f" norm rows={self.norm_rows} (1-step diffs {self.norm_inexact})"
+                   if self.norm_rows else ""))
+
+
+def ordered_bf16(bits) -> np.ndarray:
+    """bfloat16 bit patterns -> integers in the order of the values (adjacent
+    values differ by 1; +0 and -0 both map to 0)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
 
 
 def commit_band_positions(info, bound) -> set:
@@ -183,17 +195,25 @@ def compare_step(rep: Report, tag: str, before: O.CanvasState, after: O.CanvasSt
 class Lockstep:
     """Drive the HIP library and the oracle side by side on one workload."""
 
-    def __init__(self, wl, W, Hs, device, logits=False, layout=0):
+    def __init__(self, wl, W, Hs, device, logits=False, layout=0, tail: O.Tail = None):
         import torch
         from uniform_state_discrete_step_amd import dgd
         self.dgd, self.torch = dgd, torch
         self.wl, self.W, self.Hs, self.dev = wl, W, Hs, device
+        self.tail = tail
         self.Wd = torch.from_numpy(W.view(np.int16)).to(device)
         if layout == dgd.DGD_VOCAB_PACKED:
             self.Wd = dgd.pack_vocab(self.Wd, wl.V, wl.d)
         self.Hd = torch.from_numpy(Hs.view(np.int16)).to(device)
+        tkw = {}
+        if tail is not None:
+            if tail.norm_weight is not None:
+                tkw["norm_weight"] = torch.from_numpy(
+                    np.ascontiguousarray(tail.norm_weight).view(np.int16)).to(device)
+                tkw["norm_eps"] = tail.norm_eps
+            tkw["softcap"] = tail.softcap
         self.ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=device,
-                               logits=logits, vocab_layout=layout)
+                               logits=logits, vocab_layout=layout, **tkw)
         self.params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence,
                                       wl.stability_threshold, wl.freeze, wl.final_emit)
         self.P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,
@@ -234,6 +254,22 @@ class Lockstep:
             "steps_used": int(sv["steps_used"][c]),
         }
 
+    def check_norm(self, rep: Report, b: int, s_idx: int):
+        """The normalised rows the GPU wrote: within one bfloat16 step of the
+        oracle's (both round once from a float64 value; only the order of the
+        norm's sum differs)."""
+        wl = self.wl
+        g = self.ctx.norm_h.cpu().numpy().view(np.uint16).reshape(wl.B * wl.L, wl.d)
+        o = O.rms_norm(self.Hs[b, s_idx].reshape(wl.B * wl.L, wl.d), self.tail.norm_weight,
+                       self.tail.norm_eps)
+        ulp = np.abs(ordered_bf16(g) - ordered_bf16(o))
+        rep.norm_rows += g.shape[0]
+        rep.norm_inexact += int(np.count_nonzero(ulp))
+        if ulp.max() > 1:
+            r, k = np.unravel_index(int(np.argmax(ulp)), ulp.shape)
+            rep.fail(f"block {b} step {s_idx}: normalised row {r} element {k} differs by "
+                     f"{int(ulp.max())} bf16 steps (gpu {g[r, k]:#06x}, oracle {o[r, k]:#06x})")
+
     def run(self, blocks=None, steps=None, rep: Report = None, progress=None) -> Report:
         torch, wl, dgd = self.torch, self.wl, self.dgd
         rep = rep or Report()
@@ -251,10 +287,12 @@ class Lockstep:
                 dgd.dgd_step(self.Hd[b, s_idx].reshape(-1), self.Wd, self.canvas, self.committed,
                              b, s_idx, self.params, wl.seeds, self.ctx)
                 torch.cuda.synchronize()
+                if self.tail is not None and self.tail.norm_weight is not None:
+                    self.check_norm(rep, b, s_idx)
                 for c in range(wl.B):
                     before = self.states[c]
                     after, info = O.step(before, self.Hs[b, s_idx, c], self.W, b, s_idx, self.P,
-                                         wl.seeds[c], wl.bounds[c], W64=self.W64)
+                                         wl.seeds[c], wl.bounds[c], W64=self.W64, tail=self.tail)
                     compare_step(rep, f"block {b} step {s_idx} canvas {c}", before, after, info,
                                  self.pull(c), wl.L, wl.V, b, s_idx, self.P, wl.seeds[c],
                                  float(np.float32(wl.bounds[c])))

@@ -59,6 +59,10 @@ def _ctx(**kw):
     c.workspace_bytes = kw.get("workspace_bytes", 1 << 30)
     c.state = kw.get("state", FAKE)
     c.vocab_layout = kw.get("vocab_layout", 0)
+    c.norm_weight = kw.get("norm_weight", None)
+    c.norm_eps = kw.get("norm_eps", 0.0)
+    c.softcap = kw.get("softcap", 0.0)
+    c.norm_h = kw.get("norm_h", None)
     return c
 
 
@@ -129,6 +133,38 @@ def test_invalid_step_block_and_pointers_are_refused(lib):
     assert lib.dgd_debug_gumbel(None, FAKE, 4, None) == dgd.DGD_EINVAL
     assert lib.dgd_debug_gumbel(FAKE, FAKE, -1, None) == dgd.DGD_EINVAL
     assert lib.dgd_debug_gumbel(FAKE, FAKE, 0, None) == dgd.DGD_OK
+
+
+@pytest.mark.parametrize("kw", [
+    dict(softcap=-1.0),
+    dict(softcap=0.001),
+    dict(softcap=2e4),
+    dict(softcap=float("nan")),
+    dict(softcap=float("inf")),
+    dict(norm_weight=FAKE * 4),                                   # no norm_h
+    dict(norm_weight=FAKE * 4 + 2, norm_h=FAKE * 8),              # misaligned weights
+    dict(norm_weight=FAKE * 4, norm_h=FAKE * 8 + 4),              # misaligned norm_h
+    dict(norm_weight=FAKE * 4, norm_h=FAKE * 8, norm_eps=-1e-6),
+    dict(norm_weight=FAKE * 4, norm_h=FAKE * 8, norm_eps=float("nan")),
+    dict(norm_weight=FAKE * 4, norm_h=FAKE * 8, norm_eps=2.0),
+    dict(norm_weight=FAKE * 4, norm_h=FAKE),                      # norm_h overlaps H
+    dict(norm_weight=FAKE * 4, norm_h=FAKE + 16 * 64 * 2 - 16),   # ... at H's last bytes
+])
+def test_invalid_tail_is_refused(lib, kw):
+    assert _step(lib, _ctx(**kw)) == dgd.DGD_EINVAL
+    assert dgd.dgd_last_error()
+
+
+def test_tail_overlap_is_checked_over_every_step_of_a_run(lib):
+    # H_steps spans N steps of B*L*d bf16 values; norm_h just past step 0 still overlaps
+    p = dgd.make_params(N=8)
+    s = (ctypes.c_uint64 * 1)(0)
+    step_bytes = 16 * 64 * 2
+    for nh in (FAKE + step_bytes, FAKE + 8 * step_bytes - 16):
+        ctx = _ctx(norm_weight=FAKE * 64, norm_h=nh)
+        assert lib.dgd_run(FAKE, FAKE * 128, FAKE * 256, FAKE * 512, ctypes.byref(p), s,
+                           ctypes.byref(ctx)) == dgd.DGD_EINVAL
+        assert "overlaps" in dgd.dgd_last_error()
 
 
 def test_binding_refuses_missing_library(tmp_path):

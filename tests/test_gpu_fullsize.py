@@ -35,7 +35,7 @@ def dev():
 class FullRun:
     """Step a workload on the GPU with dgd_step and check every step."""
 
-    def __init__(self, wl, dev, W=None, Hs=None, layout=1, Wd=None):
+    def __init__(self, wl, dev, W=None, Hs=None, layout=1, Wd=None, tail: O.Tail = None):
         import torch
         from uniform_state_discrete_step_amd import dgd
         self.torch, self.dgd, self.wl, self.dev = torch, dgd, wl, dev
@@ -48,8 +48,15 @@ class FullRun:
                 Wd = dgd.pack_vocab(Wd, wl.V, wl.d)
         self.Wd = Wd
         self.Hd = torch.from_numpy(Hs.view(np.int16)).to(dev)
+        self.tail = tail
+        tkw = {}
+        if tail is not None:
+            if tail.norm_weight is not None:
+                tkw["norm_weight"] = torch.from_numpy(tail.norm_weight.view(np.int16)).to(dev)
+                tkw["norm_eps"] = tail.norm_eps
+            tkw["softcap"] = tail.softcap
         self.ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev,
-                               vocab_layout=layout)
+                               vocab_layout=layout, **tkw)
         self.params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence,
                                       wl.stability_threshold, wl.freeze, wl.final_emit)
         self.P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,
@@ -76,7 +83,7 @@ class FullRun:
         rng = np.random.default_rng([b, s])
         for c in range(wl.B):
             rows = np.sort(rng.choice(wl.L, size=rows_per_canvas, replace=False))
-            z = O.projection(self.Hs[b, s, c][rows], self.W, W64=self.W64)
+            z = O.logits(self.Hs[b, s, c][rows], self.W, self.tail, W64=self.W64)
             st = O.position_stats(z, T, wl.seeds[c], b * wl.L + rows, b * wl.N + s)
             sl = slice(c * wl.L, (c + 1) * wl.L)
             compare_stats(rep, f"block {b} step {s} canvas {c} rows {rows.tolist()}", st,
@@ -157,6 +164,15 @@ def test_batched_full_run_and_batch_invariance(dev):
                           run.canvas[c * wl.G:(c + 1) * wl.G].cpu().numpy())
     assert np.array_equal(solo.committed.cpu().numpy(),
                           run.committed[c * wl.G:(c + 1) * wl.G].cpu().numpy())
+
+
+def test_gemma_vocab_full_run_with_lm_head_tail(dev):
+    """Output norm + projection + softcap (c = 30) at the full size, packed table."""
+    from uniform_state_discrete_step_amd.inputs import make_norm_weight
+    wl = WORKLOADS["gemma_vocab"]
+    tail = O.Tail(norm_weight=make_norm_weight(wl.d, wl.cfg_seed), norm_eps=1e-6, softcap=30.0)
+    _check(FullRun(wl, dev, tail=tail).run(sample_every=6, rows_per_canvas=6),
+           f"{wl.name} with output norm and softcap")
 
 
 @pytest.mark.parametrize("layout", [1, 0], ids=["packed", "rows"])

@@ -12,7 +12,8 @@ import pytest
 from oracle import dgd_oracle as O
 from tests.parity import TOL_LOGIT_REL, Lockstep
 from uniform_state_discrete_step_amd.inputs import (WORKLOADS, f32_to_bf16_bits,
-                                                    make_workload_arrays, shrink)
+                                                    make_norm_weight, make_workload_arrays,
+                                                    shrink)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,13 +37,15 @@ def bf16(x):
     return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
 
 
-def run_lockstep(wl, dev, W=None, Hs=None, logits=False, layout=0, **kw):
+def run_lockstep(wl, dev, W=None, Hs=None, logits=False, layout=0, tail=None, **kw):
     if W is None:
         W, Hs = make_workload_arrays(wl, threads=8)
-    ls = Lockstep(wl, W, Hs, dev, logits=logits, layout=layout)
+    ls = Lockstep(wl, W, Hs, dev, logits=logits, layout=layout, tail=tail)
     rep = ls.run(**kw)
+    tag = "" if tail is None else (f" norm={tail.norm_weight is not None} eps={tail.norm_eps}"
+                                   f" softcap={tail.softcap}")
     print(f"\n[{wl.name} layout={layout} B={wl.B} L={wl.L} G={wl.G} V={wl.V} d={wl.d} N={wl.N} "
-          f"freeze={wl.freeze} final_emit={wl.final_emit}] {rep.summary()}", flush=True)
+          f"freeze={wl.freeze} final_emit={wl.final_emit}{tag}] {rep.summary()}", flush=True)
     assert not rep.failures, "\n".join(rep.failures)
     return ls, rep
 
@@ -102,14 +105,89 @@ def test_small_vocab_lockstep(dev, layout):
 
 
 # ----------------------------------------------------------------------------
-def _logit_check(wl, dev, W, Hs, steps, layout):
+# the lm-head tail: output RMSNorm before the projection, softcap after it
+# ----------------------------------------------------------------------------
+def _tail(wl, norm=True, eps=1e-6, softcap=30.0, wscale=(0.5, 8.0)):
+    return O.Tail(norm_weight=make_norm_weight(wl.d, wl.cfg_seed, wscale) if norm else None,
+                  norm_eps=eps, softcap=softcap)
+
+
+@pytest.mark.parametrize("tail", [
+    dict(norm=True, softcap=0.0),
+    dict(norm=False, softcap=30.0),
+    dict(norm=True, softcap=30.0),
+    dict(norm=True, softcap=5.0, eps=0.0),           # a cap that bites on most logits
+    dict(norm=True, softcap=30.0, wscale=(0.05, 0.5)),  # small weights: high entropies
+], ids=["norm", "cap30", "norm_cap30", "norm_cap5", "norm_small_w"])
+def test_tail_lockstep(dev, tail, layout):
+    wl = WORKLOADS["tiny"]
+    run_lockstep(wl, dev, layout=layout, tail=_tail(wl, **tail))
+
+
+@pytest.mark.parametrize("shape", [
+    dict(V=1001, d=72, L=37, B=3, G=74, N=5),
+    dict(V=4096, d=136, L=70, B=2, G=70, N=6),
+    dict(V=777, d=4104, L=33, B=1, G=33, N=3),     # three hidden-row passes, ragged
+], ids=["ragged", "straddle", "wide_hidden"])
+def test_tail_ragged_shapes(dev, shape, layout):
+    B = shape["B"]
+    wl = shrink(WORKLOADS["tiny"], name="ragged_tail", cfg_seed=9, seeds=tuple(range(B)),
+                bounds=tuple((0.1, 0.3, 0.05)[c % 3] for c in range(B)), **shape)
+    run_lockstep(wl, dev, layout=layout, tail=_tail(wl))
+
+
+def test_tail_small_vocab_lockstep(dev, layout):
+    wl = WORKLOADS["small_vocab"]
+    run_lockstep(wl, dev, layout=layout, tail=_tail(wl), steps=range(0, 48, 6))
+
+
+def test_norm_of_special_rows(dev):
+    """Zero rows, rows of one nonzero value, tiny and huge rows, negative
+    zeros: the normalised rows against the oracle, within one bf16 step."""
+    wl = shrink(WORKLOADS["tiny"], L=8, G=8, N=1, d=64)
+    W, Hs = make_workload_arrays(wl, threads=1)
+    x = O.bf16_to_f64(Hs[0, 0, 0]).copy()
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, 5] = -3.0
+    x[2] *= 2.0 ** -100                 # tiny rows (every input stays a normal bf16)
+    x[3] *= 2.0 ** 100
+    x[4, ::2] = 0.0
+    x[5] = 0.0                          # one huge value: the others normalise below 2^-126
+    x[5, 0], x[5, 1], x[5, 2], x[5, 3] = 2.0 ** 60, 2.0 ** -70, -(2.0 ** -72), 3 * 2.0 ** -75
+    Hs = Hs.copy()
+    Hs[0, 0, 0] = bf16(x)
+    Hs[0, 0, 0, 0, ::3] = 0x8000        # negative zeros in the zero row
+    tail = _tail(wl, eps=1e-6, softcap=0.0)
+    ls = Lockstep(wl, W, Hs, dev, tail=tail)
+    rep = ls.run()
+    print(f"\n[special rows] {rep.summary()}", flush=True)
+    assert not rep.failures, "\n".join(rep.failures)
+    g = ls.ctx.norm_h.cpu().numpy().view(np.uint16).reshape(wl.L, wl.d)
+    assert not (g[0] & 0x7FFF).any()                  # a zero row stays zero (eps > 0)
+
+
+def test_tail_logits_are_the_projection_of_the_normalised_rows(dev, layout):
+    wl = WORKLOADS["tiny"]
+    W, Hs = make_workload_arrays(wl, threads=1)
+    tail = _tail(wl, softcap=5.0)
+    z_gpu, z = _logit_check(wl, dev, W, Hs, steps=[0, 1], layout=layout, tail=tail)
+    # ctx->logits holds the projection before the cap: some logits exceed it
+    assert np.abs(z_gpu).max() > 6.0
+
+
+# ----------------------------------------------------------------------------
+def _logit_check(wl, dev, W, Hs, steps, layout, tail=None):
     import torch
-    ls = Lockstep(wl, W, Hs, dev, logits=True, layout=layout)
+    ls = Lockstep(wl, W, Hs, dev, logits=True, layout=layout, tail=tail)
     ls.run(steps=steps)
     torch.cuda.synchronize()
     z_gpu = ls.ctx.logits.cpu().numpy().reshape(wl.B * wl.L, wl.V).astype(np.float64)
     b, s = wl.blocks - 1, steps[-1]
-    z = O.projection(Hs[b, s].reshape(wl.B * wl.L, wl.d), W)
+    H_rows = Hs[b, s].reshape(wl.B * wl.L, wl.d)
+    if tail is not None and tail.norm_weight is not None:
+        H_rows = O.rms_norm(H_rows, tail.norm_weight, tail.norm_eps)
+    z = O.projection(H_rows, W)
     scale = np.maximum(np.abs(z), np.sqrt(np.mean(z * z, axis=1, keepdims=True)))
     rel = np.abs(z_gpu - z) / np.maximum(scale, 1e-30)
     print(f"\n[{wl.name}] logits: max rel err {rel.max():.3e}, max abs err "

@@ -12,7 +12,9 @@
 //   k_commit        one workgroup per canvas applies the early-stop rule,
 //                   sorts the open positions by entropy, applies the entropy
 //                   bound, writes samples and re-noises the rest.
-// plus k_init_block at the start of each block.
+// plus k_init_block at the start of each block, and, when the caller asks for
+// the lm-head tail, k_rmsnorm (the output norm, before the projection) and a
+// softcap applied to the logits inside the projection's epilogue.
 //
 // The method follows "The Annotated DiffusionGemma" walkthrough, section
 // "Sampling" (temperature, entropy, low-entropy prefix, early stop), with the
@@ -26,6 +28,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <type_traits>
 #include <vector>
 
 #include "../../include/dgd.h"
@@ -69,6 +72,7 @@ struct ProjArgs {
   int32_t P, n_vtiles, n_mtiles;
   int32_t block, gstep;
   float c2;               // log2(e) / T_s
+  float cap_in, cap_out;  // softcap: 1 / c and c * c2 (used only when the cap is on)
   uint32_t key[DGD_MAX_CANVASES][2];
 };
 
@@ -158,20 +162,40 @@ constexpr int waitcnt_enc(int vm, int lgkm) {
   return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
 }
 
+// Softcapped logit in bits: c * tanh(z / c) * log2(e) / T, given
+// cin = 1 / c and cout = c * log2(e) / T.  tanh(t) = sign(t) (1 - e) / (1 + e)
+// with e = 2^(-2 log2(e) |t|): absolute error a few 2^-24 (the cancellation in
+// 1 - e near t = 0 is absolute, not relative), then scaled by cout.
+__device__ __forceinline__ float softcap_bits(float z, float cin, float cout) {
+  const float t = z * cin;
+  const float e = fexp2(fabsf(t) * -2.8853900817779268f);
+  const float r = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
+  return copysignf(r, t) * cout;
+}
+
 // Record of one position over the 64 vocabulary ids held by a lane pair:
 // z[vb][4q + e] (lane half h) is the logit of id vbase + 32 vb + 8 q + 4 h + e.
 // The two halves' records are merged; both lanes return the merged record.
-template <bool kUniformKey>
+// kCap: the logits pass through the softcap first (c2 is then unused).
+template <bool kUniformKey, bool kCap>
 __device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int half, int V, float c2,
-                                           uint32_t pabs, uint32_t gstep, uint32_t key0,
-                                           uint32_t key1) {
+                                           float cin, float cout, uint32_t pabs, uint32_t gstep,
+                                           uint32_t key0, uint32_t key1) {
   // Tempered logits in bits, x2 = z * c2, computed once in place (a plain,
   // non-contracted multiply).  value index i = vb*16 + 4q + e  <->
   // vocabulary id vbase + vb*32 + 8q + 4h + e.  In a ragged last tile, ids
   // past V get kMasked, far below the running-max start kNeg: they add exact
   // zeros to S and A and never win the argmax or the sample.
+  if constexpr (kCap) {
 #pragma unroll
-  for (int i = 0; i < kVB * 16; ++i) z[i >> 4][i & 15] = __fmul_rn(z[i >> 4][i & 15], c2);
+    for (int i = 0; i < kVB * 16; ++i) {
+      z[i >> 4][i & 15] = softcap_bits(z[i >> 4][i & 15], cin, cout);
+      if ((i & 15) == 15) __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kVB * 16; ++i) z[i >> 4][i & 15] = __fmul_rn(z[i >> 4][i & 15], c2);
+  }
   if (vbase + kVocabPerWave > V) {
 #pragma unroll
     for (int i = 0; i < kVB * 16; ++i) {
@@ -252,8 +276,9 @@ __device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int ha
 // products summed are exactly those of the plain dot product.
 //
 // kUniformKey: every 32-row block lies inside one canvas (L % 32 == 0), so the
-// Philox key is wave-uniform and lives in scalar registers.
-template <int MB, bool kLogits, bool kUniformKey>
+// Philox key is wave-uniform and lives in scalar registers.  kCap: the logit
+// softcap is applied before the temperature.
+template <int MB, bool kLogits, bool kUniformKey, bool kCap>
 __global__ void __launch_bounds__(kPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 k_project(const ProjArgs a) {
   static_assert(MB == 2 || MB == 4 || MB == 8, "MB");
@@ -450,7 +475,8 @@ k_project(const ProjArgs a) {
         }
       }
 
-      const Rec wrec = tile_record<kUniformKey>(z, vbase, half, a.V, a.c2, pabs, (uint32_t)a.gstep, key0, key1);
+      const Rec wrec = tile_record<kUniformKey, kCap>(z, vbase, half, a.V, a.c2, a.cap_in, a.cap_out, pabs,
+                                                      (uint32_t)a.gstep, key0, key1);
       if (half == 0) {
         Rec* slot = recs + wave * PPW + pb * 32 + col;
         rec_store(slot, rec_merge(rec_load(slot), wrec));
@@ -524,7 +550,7 @@ __global__ void __launch_bounds__(kThreads) k_pack_vocab(const uint16_t* __restr
 //   * one barrier per chunk, inside MFMA step 3 (see chunk()).
 // The H stream is cyclic over the chunks, so a tile finds the first HB chunks
 // of H already in LDS.
-template <int NB, bool kLogits, bool kUniformKey, int PW, int RING, int HB>
+template <int NB, bool kLogits, bool kUniformKey, bool kCap, int PW, int RING, int HB>
 __global__ void __launch_bounds__(256 * PW) __attribute__((amdgpu_waves_per_eu(PW, PW)))
 k_project_packed(const ProjArgs a) {
   static_assert(NB == 1 || NB == 2 || NB == 4 || NB == 8, "NB");
@@ -757,7 +783,8 @@ k_project_packed(const ProjArgs a) {
             }
         }
       }
-      const Rec wrec = tile_record<kUniformKey>(z, vbase, half, a.V, a.c2, pabs, (uint32_t)a.gstep, key0, key1);
+      const Rec wrec = tile_record<kUniformKey, kCap>(z, vbase, half, a.V, a.c2, a.cap_in, a.cap_out, pabs,
+                                                      (uint32_t)a.gstep, key0, key1);
       if (half == 0) {
         Rec* slot = recs + wave * PPW + pb * 32 + col;
         rec_store(slot, rec_merge(rec_load(slot), wrec));
@@ -952,6 +979,78 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
 
 // Grid (ceil(L/4), B); one wave per position merges that position's partial
 // records (fixed order: lanes over the groups, then a butterfly).
+// ---------------------------------------------------------------------------
+// k_rmsnorm: the output norm of the final hidden states
+// ---------------------------------------------------------------------------
+// float64 -> bfloat16 bits, one rounding to nearest with ties to even.  In
+// bfloat16's normal range the double is rounded at its 45th fraction bit
+// (keeping bfloat16's 7) with an integer add on its bit pattern; the result
+// has 8 significant bits and converts to float exactly.  Below 2^-126 the
+// spacing is bfloat16's subnormal step 2^-133: scale, round to an integer
+// (rint: ties to even), scale back, all exact in double.
+__device__ inline uint16_t f64_to_bf16_rne(double v) {
+  if (fabs(v) < 0x1p-126) {
+    const double q = rint(v * 0x1p133) * 0x1p-133;
+    return (uint16_t)(__float_as_uint((float)q) >> 16);
+  }
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  u += ((1ull << 44) - 1) + ((u >> 45) & 1);
+  u &= ~((1ull << 45) - 1);
+  return (uint16_t)(__float_as_uint((float)__longlong_as_double((long long)u)) >> 16);
+}
+
+__device__ inline double bf16_f64(uint32_t bits16) {
+  return (double)__uint_as_float(bits16 << 16);
+}
+
+// One workgroup per row of H: h = w * x * sqrt(d) / (||x|| + eps), with the
+// squared norm summed in double (16-byte loads, per-lane partial sums, then a
+// butterfly and an LDS pass over the four waves), every product and the
+// quotient in double in that order, and one rounding to bfloat16.  The row is
+// read twice; the second read comes from cache.
+__global__ void __launch_bounds__(kThreads) k_rmsnorm(const uint16_t* __restrict__ H,
+                                                      const uint16_t* __restrict__ w,
+                                                      uint16_t* __restrict__ out, int d,
+                                                      double sqrt_d, double eps) {
+  __shared__ double red[kWaves];
+  const size_t row = blockIdx.x;
+  const u32x4_t* x4 = (const u32x4_t*)(H + row * d);
+  const u32x4_t* w4 = (const u32x4_t*)w;
+  u32x4_t* o4 = (u32x4_t*)(out + row * d);
+  const int n8 = d >> 3;
+  double ss = 0.0;
+  for (int k = threadIdx.x; k < n8; k += kThreads) {
+    const u32x4_t v = x4[k];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double lo = bf16_f64(v[j] & 0xffffu), hi = bf16_f64(v[j] >> 16);
+      ss = fma(lo, lo, ss);
+      ss = fma(hi, hi, ss);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) tot += red[i];
+  const double den = sqrt(tot) + eps;
+  for (int k = threadIdx.x; k < n8; k += kThreads) {
+    const u32x4_t v = x4[k], g = w4[k];
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double xl = bf16_f64(v[j] & 0xffffu), xh = bf16_f64(v[j] >> 16);
+      const double wl = bf16_f64(g[j] & 0xffffu), wh = bf16_f64(g[j] >> 16);
+      const uint32_t bl = f64_to_bf16_rne(wl * xl * sqrt_d / den);
+      const uint32_t bh = f64_to_bf16_rne(wh * xh * sqrt_d / den);
+      r[j] = bl | (bh << 16);
+    }
+    o4[k] = r;
+  }
+}
+
 __global__ void __launch_bounds__(kThreads) k_merge(const CommitArgs a) {
   const int c = blockIdx.y;
   if (a.st_done[c]) return;
@@ -1104,6 +1203,22 @@ int check_shape(const dgd_ctx* ctx) {
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
+// The optional lm-head tail; H_bytes is the extent of H (all steps for dgd_run).
+int check_tail(const dgd_ctx* ctx, const void* H, size_t H_bytes) {
+  const float c = ctx->softcap;
+  if (!std::isfinite(c) || (c != 0.f && (c < 0.01f || c > 10000.f)))
+    return fail(DGD_EINVAL, "softcap=%g must be 0 or in [0.01, 10000]", c);
+  if (!ctx->norm_weight) return DGD_OK;
+  if (!ctx->norm_h) return fail(DGD_EINVAL, "norm_weight is set but norm_h is NULL");
+  if (!aligned16(ctx->norm_weight) || !aligned16(ctx->norm_h))
+    return fail(DGD_EINVAL, "norm_weight/norm_h is not 16-byte aligned");
+  if (!finite01(ctx->norm_eps)) return fail(DGD_EINVAL, "norm_eps=%g outside [0, 1]", ctx->norm_eps);
+  const uintptr_t h0 = (uintptr_t)H, h1 = h0 + H_bytes;
+  const uintptr_t n0 = (uintptr_t)ctx->norm_h, n1 = n0 + (size_t)ctx->B * ctx->L * ctx->d * 2;
+  if (h0 < n1 && n0 < h1) return fail(DGD_EINVAL, "norm_h overlaps H");
+  return DGD_OK;
+}
+
 int check_params(const dgd_params* prm) {
   if (!prm) return fail(DGD_EINVAL, "params is NULL");
   const int N = prm->num_inference_steps;
@@ -1203,15 +1318,26 @@ struct Timer {
   }
 };
 
+// Calls f(std::integral_constant<bool, b>...) for run-time flags b...: one
+// kernel instantiation per combination.
+template <bool... Bs, typename F>
+void with_flags(F&& f) { f(std::integral_constant<bool, Bs>{}...); }
+template <bool... Bs, typename F, typename... Rest>
+void with_flags(F&& f, bool b, Rest... rest) {
+  if (b) with_flags<Bs..., true>(f, rest...);
+  else with_flags<Bs..., false>(f, rest...);
+}
+
+struct Flags {
+  bool logits, uniform, cap;
+};
+
 template <int MB>
-void launch_project_mb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits, bool uniform) {
-  if (logits) {
-    if (uniform) hipLaunchKernelGGL((k_project<MB, true, true>), grid, dim3(kPThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_project<MB, true, false>), grid, dim3(kPThreads), 0, s, a);
-  } else {
-    if (uniform) hipLaunchKernelGGL((k_project<MB, false, true>), grid, dim3(kPThreads), 0, s, a);
-    else hipLaunchKernelGGL((k_project<MB, false, false>), grid, dim3(kPThreads), 0, s, a);
-  }
+void launch_project_mb(const ProjArgs& a, dim3 grid, hipStream_t s, Flags fl) {
+  with_flags([&](auto lg, auto uni, auto cap) {
+    hipLaunchKernelGGL((k_project<MB, decltype(lg)::value, decltype(uni)::value, decltype(cap)::value>),
+                       grid, dim3(kPThreads), 0, s, a);
+  }, fl.logits, fl.uniform, fl.cap);
 }
 
 // Launch shape of the packed projection: one wave per SIMD, a two-chunk W
@@ -1222,16 +1348,13 @@ void launch_project_mb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits,
 constexpr int kPackedPW = 1, kPackedRing = 2, kPackedHB = 2;
 
 template <int NB>
-void launch_packed_nb(const ProjArgs& a, dim3 grid, hipStream_t s, bool logits, bool uniform) {
+void launch_packed_nb(const ProjArgs& a, dim3 grid, hipStream_t s, Flags fl) {
   constexpr int PW = kPackedPW, R = kPackedRing, HB = kPackedHB;
-  const dim3 block(256 * PW);
-  if (logits) {
-    if (uniform) hipLaunchKernelGGL((k_project_packed<NB, true, true, PW, R, HB>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_project_packed<NB, true, false, PW, R, HB>), grid, block, 0, s, a);
-  } else {
-    if (uniform) hipLaunchKernelGGL((k_project_packed<NB, false, true, PW, R, HB>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_project_packed<NB, false, false, PW, R, HB>), grid, block, 0, s, a);
-  }
+  with_flags([&](auto lg, auto uni, auto cap) {
+    hipLaunchKernelGGL((k_project_packed<NB, decltype(lg)::value, decltype(uni)::value,
+                                         decltype(cap)::value, PW, R, HB>),
+                       grid, dim3(256 * PW), 0, s, a);
+  }, fl.logits, fl.uniform, fl.cap);
 }
 
 int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* committed,
@@ -1247,6 +1370,14 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   const int gstep = block * N + step;
   const double T = (double)prm->t_max + ((double)step / N) * ((double)prm->t_min - prm->t_max);
 
+  if (ctx->norm_weight) {
+    hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(kThreads), 0, stream, H, ctx->norm_weight,
+                       ctx->norm_h, dd, std::sqrt((double)dd), (double)ctx->norm_eps);
+    const hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return hip_fail(e0, "k_rmsnorm launch");
+    H = ctx->norm_h;
+  }
+
   ProjArgs pa{};
   pa.H = H; pa.W = W;
   pa.part = (Rec*)(ws + wl.part);
@@ -1257,9 +1388,13 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   pa.n_vtiles = num_vtiles(V);
   pa.block = block; pa.gstep = gstep;
   pa.c2 = (float)(kLog2e / T);
+  const bool cap = ctx->softcap != 0.f;
+  if (cap) {
+    pa.cap_in = (float)(1.0 / ctx->softcap);
+    pa.cap_out = (float)(ctx->softcap * kLog2e / T);
+  }
   fill_keys(pa.key, seed, B);
-  const bool lg = ctx->logits != nullptr;
-  const bool uni = (L % 32) == 0;
+  const Flags fl{ctx->logits != nullptr, (L % 32) == 0, cap};
   int rc;
   if (ctx->vocab_layout == DGD_VOCAB_PACKED) {
     const int NB = M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8;
@@ -1267,10 +1402,10 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
     const dim3 grid1(pa.n_mtiles * pa.P);
     if ((rc = timer.begin(stream))) return rc;
     switch (NB) {
-      case 1: launch_packed_nb<1>(pa, grid1, stream, lg, uni); break;
-      case 2: launch_packed_nb<2>(pa, grid1, stream, lg, uni); break;
-      case 4: launch_packed_nb<4>(pa, grid1, stream, lg, uni); break;
-      default: launch_packed_nb<8>(pa, grid1, stream, lg, uni); break;
+      case 1: launch_packed_nb<1>(pa, grid1, stream, fl); break;
+      case 2: launch_packed_nb<2>(pa, grid1, stream, fl); break;
+      case 4: launch_packed_nb<4>(pa, grid1, stream, fl); break;
+      default: launch_packed_nb<8>(pa, grid1, stream, fl); break;
     }
   } else {
     const int MB = M <= 64 ? 2 : M <= 128 ? 4 : 8;
@@ -1278,9 +1413,9 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
     const dim3 grid1(pa.n_mtiles * pa.P);
     if ((rc = timer.begin(stream))) return rc;
     switch (MB) {
-      case 2: launch_project_mb<2>(pa, grid1, stream, lg, uni); break;
-      case 4: launch_project_mb<4>(pa, grid1, stream, lg, uni); break;
-      default: launch_project_mb<8>(pa, grid1, stream, lg, uni); break;
+      case 2: launch_project_mb<2>(pa, grid1, stream, fl); break;
+      case 4: launch_project_mb<4>(pa, grid1, stream, fl); break;
+      default: launch_project_mb<8>(pa, grid1, stream, fl); break;
     }
   }
   hipError_t e = hipGetLastError();
@@ -1359,6 +1494,7 @@ int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_
   if ((rc = check_workspace(ctx))) return rc;
   if (!H || !W_vocab || !canvas || !committed) return fail(DGD_EINVAL, "H/W_vocab/canvas/committed is NULL");
   if (!aligned16(H) || !aligned16(W_vocab)) return fail(DGD_EINVAL, "H/W_vocab is not 16-byte aligned");
+  if ((rc = check_tail(ctx, H, (size_t)ctx->B * ctx->L * ctx->d * 2))) return rc;
   if (block < 0 || block >= ctx->G / ctx->L)
     return fail(DGD_EINVAL, "block=%d outside [0, %d)", block, ctx->G / ctx->L);
   if (step < 0 || step >= params->num_inference_steps)
@@ -1385,6 +1521,7 @@ int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas, u
   const int N = params->num_inference_steps;
   const int blocks = ctx->G / ctx->L;
   const size_t step_elems = (size_t)ctx->B * ctx->L * ctx->d;
+  if ((rc = check_tail(ctx, H_steps, (size_t)blocks * N * step_elems * 2))) return rc;
   Timer timer;
   timer.on = ctx->k1_ms != nullptr;
   for (int b = 0; b < blocks && rc == DGD_OK; ++b) {

@@ -66,6 +66,10 @@ class DgdCtx(ctypes.Structure):
         ("k1_ms", ctypes.POINTER(ctypes.c_double)),
         ("k1_launches", ctypes.POINTER(ctypes.c_int32)),
         ("vocab_layout", ctypes.c_int32),
+        ("norm_weight", ctypes.c_void_p),
+        ("norm_eps", ctypes.c_float),
+        ("softcap", ctypes.c_float),
+        ("norm_h", ctypes.c_void_p),
     ]
 
 
@@ -151,7 +155,11 @@ class Context:
     """
 
     def __init__(self, B, L, V, d, G, bounds, device="cuda", outputs=True, logits=False,
-                 commit_trace=False, vocab_layout=DGD_VOCAB_ROWS):
+                 commit_trace=False, vocab_layout=DGD_VOCAB_ROWS, norm_weight=None,
+                 norm_eps=0.0, softcap=0.0):
+        """norm_weight: optional device int16[d] (bf16 bits) output-norm weights;
+        when given, ``norm_h`` (int16[B*L*d]) receives the normalised rows each
+        step.  softcap: the logit cap c (0 = none)."""
         import torch
         lib = load_library()
         self.B, self.L, self.V, self.d, self.G = int(B), int(L), int(V), int(d), int(G)
@@ -178,6 +186,11 @@ class Context:
         self._k1_n = ctypes.c_int32(0)
         self.time_k1 = False
         self.vocab_layout = int(vocab_layout)
+        self.norm_weight = norm_weight
+        self.norm_eps = float(norm_eps)
+        self.softcap = float(softcap)
+        self.norm_h = (torch.empty(BL * self.d, dtype=torch.int16, device=device)
+                       if norm_weight is not None else None)
 
     def state_views(self) -> dict:
         B, BL = self.B, self.B * self.L
@@ -212,6 +225,10 @@ class Context:
         c.logits = _ptr(self.logits)
         c.commit_step = _ptr(self.commit_step)
         c.vocab_layout = self.vocab_layout
+        c.norm_weight = _ptr(self.norm_weight)
+        c.norm_eps = self.norm_eps
+        c.softcap = self.softcap
+        c.norm_h = _ptr(self.norm_h)
         if self.time_k1:
             c.k1_ms = ctypes.pointer(self._k1_ms)
             c.k1_launches = ctypes.pointer(self._k1_n)

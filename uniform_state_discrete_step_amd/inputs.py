@@ -18,6 +18,9 @@ tied [V x d] embedding table):
   ``default_rng([cfg_seed, 1, c, b*N + s])``; first L log-uniform row scales
   ``r = exp(U(ln lo, ln hi))``, then an [L, d] float32 standard normal; the row
   is ``r * z`` rounded to bfloat16.
+* Output-norm weights [d] (only for runs with the lm-head tail): generator
+  ``default_rng([cfg_seed, 2])``, log-uniform per channel in [lo, hi] (default
+  [0.5, 8]), rounded to bfloat16.  The walkthrough prints no trained values.
 
 bfloat16 values are carried as ``numpy.uint16`` bit patterns.
 """
@@ -157,3 +160,11 @@ def make_workload_arrays(wl: Workload, threads: int = 8):
 def shrink(wl: Workload, **kw) -> Workload:
     """Copy of a workload with some fields replaced (for edge-case tests)."""
     return dataclasses.replace(wl, **kw)
+
+
+def make_norm_weight(d: int, cfg_seed: int, scale=(0.5, 8.0)) -> np.ndarray:
+    """Output-norm weights [d] as bfloat16 bits (see module docstring)."""
+    rng = np.random.default_rng([cfg_seed, 2])
+    lo, hi = scale
+    w = np.exp(rng.uniform(math.log(lo), math.log(hi), size=d)).astype(np.float32)
+    return f32_to_bf16_bits(w)
