@@ -53,6 +53,13 @@ pages this work follows; citations give page and section):
 8. A new block starts from uniform tokens (Philox word 0 of counter
    (0, p_abs, block, 2)); earlier blocks are never touched; the schedule
    restarts for each block (node page, gen_length row).
+9. Self-conditioning input for the next forward (walkthrough, "Complete
+   DiffusionGemma model" and "Denoise, stage, commit, and generate": the
+   decoder receives the previous step's tempered probabilities P and forms
+   (P @ W_embed) * sqrt(hidden), with P cast to the model dtype; TensorSharp
+   doc, self-conditioning top-K cutoff, default 32): the K most probable
+   tokens of each position (ties by lower id) with their exact probabilities
+   (not renormalised), and the embedding sum over those K only.
 
 All functions below are deliberately direct: one pass per definition, no
 blocking, fusion or streaming.  Every function is pinned by the CPU tests.
@@ -288,6 +295,37 @@ def position_stats(z: np.ndarray, T: float, seed: int, p_abs, gstep: int) -> dic
         "y2": y2,
         "gap": y1 - y2,
     }
+
+
+# ----------------------------------------------------------------------------
+# 9. self-conditioning: top-K of the tempered distribution, and its embedding
+# ----------------------------------------------------------------------------
+def sc_topk(z: np.ndarray, T: float, K: int):
+    """The K most probable tokens of softmax(z / T) per row.
+
+    Order: probability descending, then id ascending (equal logits give equal
+    probabilities; the lower id comes first).  Returns (prob float64 [rows, K],
+    ids int64 [rows, K], x float64 [rows, V] the tempered logits, for bands).
+    """
+    x = np.asarray(z, dtype=np.float64) / T
+    rows, V = x.shape
+    ids = np.empty((rows, K), dtype=np.int64)
+    for r in range(rows):
+        order = np.lexsort((np.arange(V), -x[r]))       # last key is primary
+        ids[r] = order[:K]
+    m = x.max(axis=1, keepdims=True)
+    lse = m + np.log(np.exp(x - m).sum(axis=1, keepdims=True))
+    prob = np.exp(np.take_along_axis(x, ids, axis=1) - lse)
+    return prob, ids, x
+
+
+def sc_embed(prob: np.ndarray, ids: np.ndarray, W_bits: np.ndarray, scale: float) -> np.ndarray:
+    """scale * sum_j bf16(prob_j) * E[id_j] per row, float64, rounded once to
+    bfloat16.  prob [rows, K] (float32 or float64), ids [rows, K], W_bits the
+    tied table [V, d] as bf16 bits; returns bf16 bits [rows, d]."""
+    p16 = bf16_to_f64(round_bf16(np.asarray(prob, dtype=np.float64)))
+    E = bf16_to_f64(W_bits[np.asarray(ids, dtype=np.int64)])     # [rows, K, d]
+    return round_bf16(float(scale) * (p16[:, :, None] * E).sum(axis=1))
 
 
 # ----------------------------------------------------------------------------

@@ -301,6 +301,88 @@ def test_step_with_softcap_keeps_the_argmax():
 
 
 # ----------------------------------------------------------------------------
+# self-conditioning: top-K and the embedding sum
+# ----------------------------------------------------------------------------
+def test_sc_topk_two_level_closed_form():
+    # k ids at logit a, the rest at b: the k high ids come first (by id), then
+    # the lowest low ids; probabilities e^a / (k e^a + (V - k) e^b)
+    V, k, a, b, T = 50, 3, 2.0, -1.0, 0.5
+    z = np.full((1, V), b)
+    hi = [7, 31, 44]
+    z[0, hi] = a
+    prob, ids, _ = O.sc_topk(z, T, 5)
+    assert ids[0].tolist() == hi + [0, 1]
+    den = k * math.exp(a / T) + (V - k) * math.exp(b / T)
+    assert np.allclose(prob[0, :3], math.exp(a / T) / den, rtol=1e-14)
+    assert np.allclose(prob[0, 3:], math.exp(b / T) / den, rtol=1e-14)
+
+
+def test_sc_topk_uniform_row_and_full_k():
+    V = 40
+    prob, ids, _ = O.sc_topk(np.zeros((2, V)), 0.7, V)
+    assert np.array_equal(ids, np.tile(np.arange(V), (2, 1)))     # all tied: by id
+    assert np.allclose(prob, 1.0 / V, rtol=1e-15)
+    rng = np.random.default_rng(8)
+    z = rng.standard_normal((4, V)) * 3
+    prob, ids, _ = O.sc_topk(z, 0.4, V)
+    assert np.allclose(prob.sum(axis=1), 1.0, rtol=1e-13)          # K = V: the whole law
+    assert np.all(np.diff(prob, axis=1) <= 0)
+    for r in range(4):
+        assert sorted(ids[r].tolist()) == list(range(V))
+
+
+def test_sc_topk_follows_a_permutation_and_ignores_shifts():
+    rng = np.random.default_rng(9)
+    V, K = 300, 32
+    z = rng.standard_normal((3, V)) * 4
+    prob, ids, _ = O.sc_topk(z, 0.6, K)
+    perm = rng.permutation(V)                    # new id of old id v is perm[v]
+    zp = np.empty_like(z)
+    zp[:, perm] = z
+    prob_p, ids_p, _ = O.sc_topk(zp + 17.0, 0.6, K)
+    assert np.array_equal(ids_p, perm[ids])      # continuous logits: no ties
+    assert np.allclose(prob_p, prob, rtol=1e-12)
+    # the top-K probabilities are the largest K of softmax, so they bound the rest
+    p_all = np.exp(z / 0.6 - (z / 0.6).max(axis=1, keepdims=True))
+    p_all /= p_all.sum(axis=1, keepdims=True)
+    for r in range(3):
+        rest = np.delete(p_all[r], ids[r])
+        assert rest.max() <= prob[r, -1]
+
+
+def test_sc_embed_one_hot_and_identity_table():
+    rng = np.random.default_rng(10)
+    V, d = 16, 16
+    W = bf16(rng.standard_normal((V, d)))
+    # K = 1 with probability 1: the scaled embedding row itself
+    out = O.sc_embed(np.array([[1.0], [1.0]]), np.array([[3], [12]]), W, 4.0)
+    assert np.array_equal(out, bf16(O.bf16_to_f64(W[[3, 12]]) * 4.0))
+    # identity table: row r reads back scale * bf16(p) at each id
+    I = bf16(np.eye(V))
+    p = np.array([[0.5, 0.3, 0.15, 0.05]])
+    idx = np.array([[9, 2, 14, 0]])
+    out = O.bf16_to_f64(O.sc_embed(p, idx, I, 2.0))[0]
+    expect = np.zeros(V)
+    expect[idx[0]] = 2.0 * O.bf16_to_f64(bf16(p[0]))
+    assert np.array_equal(out, O.bf16_to_f64(bf16(expect)))
+
+
+def test_sc_embed_is_exact_on_dyadic_inputs():
+    # dyadic probabilities and small-integer embeddings: every product and sum
+    # is exact, so the result is the integer combination itself
+    rng = np.random.default_rng(12)
+    V, d, K = 64, 24, 4
+    Wi = rng.integers(-3, 4, size=(V, d))
+    W = bf16(Wi)
+    p = np.array([[0.5, 0.25, 0.125, 0.0625]] * 2)
+    idx = np.array([[5, 17, 33, 60], [0, 1, 2, 3]])
+    out = O.bf16_to_f64(O.sc_embed(p, idx, W, 8.0))
+    for r in range(2):
+        ref = 8.0 * sum(p[r, j] * Wi[idx[r, j]] for j in range(K))
+        assert np.array_equal(out[r], ref)
+
+
+# ----------------------------------------------------------------------------
 # entropy and argmax
 # ----------------------------------------------------------------------------
 def test_entropy_of_uniform_row_is_log_v(golden_dir):
