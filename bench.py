@@ -6,10 +6,11 @@ re-noise) over one batch of canvases.  Inputs are seeded synthetic tensors
 resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma_vocab]
-                    [--no-cpu-baseline] [--profile-only] [--lm-head-tail]
+                    [--no-cpu-baseline] [--profile-only] [--lm-head-tail] [--sc-topk K]
 
 ``--lm-head-tail`` adds the model's output norm before the projection and the
-logit softcap (c = 30) after it.
+logit softcap (c = 30) after it; ``--sc-topk K`` adds the self-conditioning
+top-K of every position (and its embedding sum) to each step.
 
 Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the fused
 projection), timed with HIP events on the library's stream in a separate
@@ -55,8 +56,8 @@ def measured_traffic(kernel):
     return rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
 
 
-def cpu_baseline(wl, W, Hs, tail=None):
-    """Time the oracle (as it stands) on one full step of the workload."""
+def cpu_baseline(wl, W, Hs, tail=None, sc_topk=0):
+    """Time the oracle (as it stands) on a few full steps of the workload."""
     from oracle import dgd_oracle as O
     try:
         from threadpoolctl import threadpool_info
@@ -66,13 +67,16 @@ def cpu_baseline(wl, W, Hs, tail=None):
     P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,
                  stability_threshold=wl.stability_threshold, freeze=wl.freeze,
                  final_emit=wl.final_emit)
-    steps = 5
+    steps = 2 if sc_topk else 5
     t0 = time.perf_counter()
     for c in range(wl.B):
         st = O.init_block(O.new_state(wl.G, wl.L), 0, wl.L, wl.V, wl.seeds[c])
         for s in range(steps):
-            st, _ = O.step(st, Hs[0, s, c], W, 0, s, P, wl.seeds[c], wl.bounds[c],
-                           tail=None if tail is None else O.Tail(**tail))
+            st, info = O.step(st, Hs[0, s, c], W, 0, s, P, wl.seeds[c], wl.bounds[c],
+                              tail=None if tail is None else O.Tail(**tail))
+            if sc_topk:
+                prob, ids, _ = O.sc_topk(info["z"], info["T"], sc_topk)
+                O.sc_embed(prob, ids, W, math.sqrt(wl.d))
     dt = time.perf_counter() - t0
     cpu_model = ""
     try:
@@ -105,6 +109,8 @@ def main():
     ap.add_argument("--lm-head-tail", action="store_true",
                     help="output RMSNorm (eps 1e-6) before the projection and a logit softcap "
                          "(c = 30) after it")
+    ap.add_argument("--sc-topk", type=int, default=0,
+                    help="self-conditioning top-K per position (0 = off), plus the embedding sum")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed loop (for rocprofv3 runs)")
@@ -129,11 +135,14 @@ def main():
     W, Hs = make_workload_arrays(wl, threads=16)
     log(f"[bench] generated {wl.name} inputs in {time.perf_counter() - t0:.1f}s")
     Wd = torch.from_numpy(W.view(np.int16)).to(dev)
+    W_rows = Wd
     layout = dgd.DGD_VOCAB_PACKED if args.layout == "packed" else dgd.DGD_VOCAB_ROWS
     if layout == dgd.DGD_VOCAB_PACKED:
         # one-time rewrite of the table into the projection's streaming order
         Wd = dgd.pack_vocab(Wd, wl.V, wl.d)
         torch.cuda.synchronize()
+    if not args.sc_topk:
+        W_rows = None    # the row-major copy only serves the self-conditioning gather
     Hd = torch.from_numpy(Hs.view(np.int16)).to(dev)
     tail, tkw = None, {}
     if args.lm_head_tail:
@@ -142,7 +151,9 @@ def main():
         tkw = {"norm_weight": torch.from_numpy(tail["norm_weight"].view(np.int16)).to(dev),
                "norm_eps": tail["norm_eps"], "softcap": tail["softcap"]}
     ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev, outputs=False,
-                      vocab_layout=layout, **tkw)
+                      vocab_layout=layout, sc_topk=args.sc_topk, **tkw)
+    sc_out = (torch.empty(wl.B * wl.L * wl.d, dtype=torch.int16, device=dev)
+              if args.sc_topk else None)
     params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence, wl.stability_threshold,
                              wl.freeze, wl.final_emit)
     canvas = torch.zeros(wl.B * wl.G, dtype=torch.int32, device=dev)
@@ -159,6 +170,12 @@ def main():
             if s == 0:
                 dgd.dgd_init_block(canvas, committed, b, params, wl.seeds, ctx)
             dgd.dgd_step(Hd[b, s].reshape(-1), Wd, canvas, committed, b, s, params, wl.seeds, ctx)
+            if sc_out is not None:
+                # the gather reads whole table rows: the row-major copy serves it
+                # (16 contiguous bytes per row per thread; the packed table would
+                # scatter them over 64-byte lines)
+                dgd.dgd_sc_embed(ctx.sc_prob, ctx.sc_id, wl.B * wl.L, args.sc_topk, W_rows,
+                                 dgd.DGD_VOCAB_ROWS, wl.V, wl.d, math.sqrt(wl.d), sc_out)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -212,8 +229,8 @@ def main():
             {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": mfma_frac})
     kname = "k_project_packed" if layout == dgd.DGD_VOCAB_PACKED else "k_project"
-    traffic = (measured_traffic(kname) if wl.name == "gemma_vocab" and not args.lm_head_tail
-               else None)
+    traffic = (measured_traffic(kname)
+               if wl.name == "gemma_vocab" and not args.lm_head_tail and not args.sc_topk else None)
     roof.update({"traffic": traffic,
                  "kernel": kname, "kernel_avg_us": k1_avg_s * 1e6,
                  "kernel_launches": k1_n, "algorithmic_bytes_per_launch": alg_bytes,
@@ -239,7 +256,8 @@ def main():
                    "hidden": wl.d, "gen_length": wl.G, "num_inference_steps": wl.N,
                    "vocab_layout": args.layout,
                    "lm_head_tail": ({"norm_eps": 1e-6, "softcap": 30.0} if args.lm_head_tail
-                                    else None)},
+                                    else None),
+                   "sc_topk": args.sc_topk},
         "logit_elems_per_s": steps_per_s * M * wl.V,
         "ms_per_step_segments": {"n": n_seg, "median": seg_ms_per_step[n_seg // 2],
                                  "min": seg_ms_per_step[0], "max": seg_ms_per_step[-1]},
@@ -248,7 +266,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on one step")
-        out["cpu_baseline"] = cpu_baseline(wl, W, Hs, tail)
+        out["cpu_baseline"] = cpu_baseline(wl, W, Hs, tail, args.sc_topk)
     print(json.dumps(out), flush=True)
 
 

@@ -80,7 +80,10 @@ typedef uint16_t dgd_bf16;
 
 /* Layouts of the vocabulary table W_vocab accepted by dgd_step / dgd_run. */
 #define DGD_VOCAB_ROWS   0  /* [V][d] row-major: the tied embedding table as is          */
-#define DGD_VOCAB_PACKED 1  /* the output of dgd_pack_vocab() (MFMA fragment order)      */
+#define DGD_VOCAB_PACKED 1
+
+/* Largest self-conditioning top-K (dgd_ctx.sc_topk, dgd_sc_embed). */
+#define DGD_SC_MAX_TOPK 32  /* the output of dgd_pack_vocab() (MFMA fragment order)      */
 
 /* Sampler knobs (node page "Inputs"; TensorSharp doc "3. Sampler contract").
  * Ranges are checked on every call:
@@ -144,6 +147,21 @@ typedef struct dgd_params {
  *   softcap      c: the logits become c * tanh(z / c) before the
  *                temperature; 0 = no cap, else in [0.01, 10000]
  * ctx->logits stays the projection z itself, before cap and temperature.
+ * Optional self-conditioning outputs (walkthrough, "Complete DiffusionGemma
+ * model" and "Denoise, stage, commit, and generate": the next forward takes
+ * this step's tempered probabilities; TensorSharp doc: self-conditioning
+ * top-K cutoff, default 32).  Needs vocab_layout = DGD_VOCAB_PACKED.
+ *   sc_topk    K in [1, DGD_SC_MAX_TOPK], K <= V; 0 = off
+ *   sc_prob    device float[B*L*K]: the K largest probabilities of
+ *              softmax(z'/T_s) per position (z' the capped logits when the
+ *              softcap is on), best first, ties by the lower id; exact
+ *              probabilities, not renormalised over the K
+ *   sc_id      device int32[B*L*K]: their vocabulary ids
+ *   sc_status  device int32[B*L] or NULL: per position, how many parts of the
+ *              vocabulary the selection recomputed exactly (0 almost always),
+ *              or -1 if its recomputation budget ran out (the K ids are then
+ *              the best found, not certified; ids of -1 mark empty slots)
+ * Positions of canvases that are done are not written.
  * Optional host outputs (timing): when k1_ms is not NULL the call records HIP
  * events around every launch of the fused projection kernel, synchronises
  * before returning, and writes the summed kernel time in ms to *k1_ms and the
@@ -168,6 +186,10 @@ typedef struct dgd_ctx {
   float    norm_eps;
   float    softcap;
   dgd_bf16* norm_h;             /* normalised H (scratch the caller owns) */
+  int32_t  sc_topk;             /* self-conditioning top-K, 0 = off */
+  float*   sc_prob;
+  int32_t* sc_id;
+  int32_t* sc_status;
 } dgd_ctx;
 
 /* State layout (device, int32/float words, in this order):
@@ -216,6 +238,21 @@ int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_
 int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas,
             uint8_t* committed, const dgd_params* params, const uint64_t* seed,
             const dgd_ctx* ctx);
+
+/* The self-conditioning input of the next forward from a step's top-K
+ * (walkthrough, "Complete DiffusionGemma model": the decoder adds
+ * (P @ W_embed) * sqrt(hidden), with P cast to the model dtype):
+ *   out[r][k] = bf16( scale * sum_{j<K} bf16(sc_prob[r][j]) * E[sc_id[r][j]][k] )
+ * summed in fp32 in j order; bf16() rounds to nearest, ties to even.  Ids
+ * outside [0, V) are skipped.
+ *   sc_prob, sc_id  device float/int32[rows*K] (as dgd_step writes them)
+ *   W_vocab         device, the table in vocab_layout (rows or packed), 16-B aligned
+ *   scale           finite; the walkthrough's embed scale is sqrt(d)
+ *   out             device bf16[rows*d], 16-byte aligned, written
+ * Enqueued on `stream`; 0 or a negative DGD_E* code. */
+int dgd_sc_embed(const float* sc_prob, const int32_t* sc_id, int32_t rows, int32_t K,
+                 const dgd_bf16* W_vocab, int32_t vocab_layout, int32_t V, int32_t d, float scale,
+                 dgd_bf16* out, void* stream);
 
 /* Size in bytes of the packed vocabulary table for (V, d):
  * ceil(V/64)*64 * ceil(d/64)*64 * 2; 0 if V or d is outside the limits. */

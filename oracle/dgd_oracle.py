@@ -474,6 +474,7 @@ def step(state: CanvasState, H_bits: np.ndarray, W_bits: np.ndarray, block: int,
     stats = position_stats(z, T, seed, block * L + np.arange(L), block * params.N + step_idx)
     new, info = step_from_stats(state, stats, block, step_idx, L, V, params, seed, bound)
     info["T"] = T
+    info["z"] = z
     return new, info
 
 

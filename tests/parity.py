@@ -17,7 +17,12 @@ fixes for bf16 inputs with fp32 accumulation):
   within 1e-5 of the bound;
 * the early-stop decision equal unless |mean entropy - confidence| < 1e-5 or
   an argmax band event moved the stability test;
-* re-noised and initial tokens bit-exact (pure integer functions).
+* re-noised and initial tokens bit-exact (pure integer functions);
+* self-conditioning top-K: the same ids unless an id's oracle tempered logit
+  is within 1e-4 of the K-th one (the sample band: both rest on the same fp32
+  logits), listed best first up to that band, probabilities within 1e-3
+  relative (the entropy bar: an error of e nats in x - lse moves p by e) or
+  1e-30 absolute (float32 probabilities flush below its normal range).
 Band events are counted, never hidden.
 """
 from __future__ import annotations
@@ -34,6 +39,9 @@ BAND_SAMPLE = 1e-4
 BAND_COMMIT = 1e-5
 BAND_CONV = 1e-5
 TOL_LOGIT_REL = 2e-2
+BAND_SC = 1e-4
+TOL_SC_PROB_REL = 1e-3
+TOL_SC_PROB_ABS = 1e-30
 
 
 @dataclasses.dataclass
@@ -49,6 +57,9 @@ class Report:
     accepted: int = 0
     norm_rows: int = 0
     norm_inexact: int = 0
+    sc_rows: int = 0
+    sc_band: int = 0
+    sc_recomputed: int = 0
     failures: list = dataclasses.field(default_factory=list)
 
     def fail(self, msg):
@@ -61,7 +72,9 @@ class Report:
                 f"commit={self.commit_band} convergence={self.conv_band} "
                 f"accepted={self.accepted} renoised={self.renoised}"
                 + (f" norm rows={self.norm_rows} (1-step diffs {self.norm_inexact})"
-                   if self.norm_rows else ""))
+                   if self.norm_rows else "")
+                + (f" sc rows={self.sc_rows} band={self.sc_band} recomputed parts="
+                   f"{self.sc_recomputed}" if self.sc_rows else ""))
 
 
 def ordered_bf16(bits) -> np.ndarray:
@@ -113,6 +126,38 @@ def compare_stats(rep: Report, tag: str, st: dict, H_gpu, A_gpu, T_gpu, rows=Non
             rep.fail(f"{tag}: token differs at row {i if rows is None else rows[i]} "
                      f"(gpu {T_gpu[i]}, oracle {T_o[i]}, gap {st['gap'][i]:.3e})")
     return set(am.tolist()), set(tm.tolist())
+
+
+def compare_sc(rep: Report, tag: str, z, T: float, K: int, prob_gpu, id_gpu, status_gpu=None,
+               rows=None):
+    """Self-conditioning top-K of the GPU against the oracle's, row by row."""
+    prob_o, ids_o, x = O.sc_topk(z, T, K)
+    for r in range(z.shape[0]):
+        rt = r if rows is None else rows[r]
+        rep.sc_rows += 1
+        if status_gpu is not None:
+            if status_gpu[r] < 0:
+                rep.fail(f"{tag} row {rt}: self-conditioning recomputation budget ran out")
+            rep.sc_recomputed += int(max(status_gpu[r], 0))
+        g, o = [int(v) for v in id_gpu[r]], [int(v) for v in ids_o[r]]
+        if any(v < 0 or v >= x.shape[1] for v in g):
+            rep.fail(f"{tag} row {rt}: invalid self-conditioning id in {g}")
+            continue
+        xk = x[r, o[-1]]
+        diff = set(g) ^ set(o)
+        for v in diff:
+            if abs(x[r, v] - xk) <= BAND_SC:
+                rep.sc_band += 1
+            else:
+                rep.fail(f"{tag} row {rt}: top-{K} id {v} differs (x {x[r, v]:.6f}, K-th {xk:.6f})")
+        xs = x[r, g]
+        if np.any(xs[1:] > xs[:-1] + BAND_SC):
+            rep.fail(f"{tag} row {rt}: top-{K} not in descending order")
+        po = dict(zip(o, prob_o[r]))
+        for j, v in enumerate(g):
+            if v in po and abs(prob_gpu[r, j] - po[v]) > TOL_SC_PROB_REL * po[v] + TOL_SC_PROB_ABS:
+                rep.fail(f"{tag} row {rt}: probability of id {v}: gpu {prob_gpu[r, j]:.6e}, "
+                         f"oracle {po[v]:.6e}")
 
 
 def compare_step(rep: Report, tag: str, before: O.CanvasState, after: O.CanvasState, info: dict,
@@ -195,7 +240,7 @@ def compare_step(rep: Report, tag: str, before: O.CanvasState, after: O.CanvasSt
 class Lockstep:
     """Drive the HIP library and the oracle side by side on one workload."""
 
-    def __init__(self, wl, W, Hs, device, logits=False, layout=0, tail: O.Tail = None):
+    def __init__(self, wl, W, Hs, device, logits=False, layout=0, tail: O.Tail = None, sc_topk=0):
         import torch
         from uniform_state_discrete_step_amd import dgd
         self.dgd, self.torch = dgd, torch
@@ -212,8 +257,10 @@ class Lockstep:
                     np.ascontiguousarray(tail.norm_weight).view(np.int16)).to(device)
                 tkw["norm_eps"] = tail.norm_eps
             tkw["softcap"] = tail.softcap
+        self.sc_topk = sc_topk
         self.ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=device,
-                               logits=logits, vocab_layout=layout, **tkw)
+                               logits=logits, vocab_layout=layout, sc_topk=sc_topk,
+                               sc_status=sc_topk > 0, **tkw)
         self.params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence,
                                       wl.stability_threshold, wl.freeze, wl.final_emit)
         self.P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,
@@ -296,6 +343,13 @@ class Lockstep:
                     compare_step(rep, f"block {b} step {s_idx} canvas {c}", before, after, info,
                                  self.pull(c), wl.L, wl.V, b, s_idx, self.P, wl.seeds[c],
                                  float(np.float32(wl.bounds[c])))
+                    if self.sc_topk and not info.get("skipped"):
+                        K, sl = self.sc_topk, slice(c * wl.L, (c + 1) * wl.L)
+                        compare_sc(rep, f"block {b} step {s_idx} canvas {c}", info["z"],
+                                   info["T"], K,
+                                   self.ctx.sc_prob.cpu().numpy().reshape(-1, K)[sl],
+                                   self.ctx.sc_id.cpu().numpy().reshape(-1, K)[sl],
+                                   self.ctx.sc_status.cpu().numpy()[sl])
                     self.states[c] = after
                 if progress:
                     progress(b, s_idx, rep)

@@ -37,10 +37,11 @@ def test_state_and_workspace_sizes(lib):
     assert dgd.dgd_state_bytes(1, 256) == (256 + 7) * 4
     assert dgd.dgd_state_bytes(8, 256) == (8 * 256 + 56) * 4
     assert dgd.dgd_state_bytes(0, 16) == 0
-    # 256 positions x 256 vocabulary groups x 32-byte records dominate
+    # 256 positions x 256 vocabulary groups x (32-byte record + 16 x 8-byte
+    # self-conditioning candidates) dominate
     ws = dgd.dgd_workspace_bytes(1, 256, 262144, 2816)
-    assert 256 * 256 * 32 <= ws <= 256 * 256 * 32 + 8192
-    assert dgd.dgd_workspace_bytes(1, 16, 1024, 64) >= 16 * 4 * 32   # V=1024: 4 groups
+    assert 256 * 256 * (32 + 128) <= ws <= 256 * 256 * (32 + 128) + 16384
+    assert dgd.dgd_workspace_bytes(1, 16, 1024, 64) >= 16 * 4 * (32 + 128)   # V=1024: 4 groups
     for bad in [(0, 16, 1024, 64), (65, 16, 1024, 64), (1, 4097, 1024, 64), (1, 16, 0, 64),
                 (1, 16, 1024, 60), (1, 16, 1024, 0), (1, 16, (1 << 24) + 1, 64)]:
         assert dgd.dgd_workspace_bytes(*bad) == 0, bad
@@ -63,6 +64,10 @@ def _ctx(**kw):
     c.norm_eps = kw.get("norm_eps", 0.0)
     c.softcap = kw.get("softcap", 0.0)
     c.norm_h = kw.get("norm_h", None)
+    c.sc_topk = kw.get("sc_topk", 0)
+    c.sc_prob = kw.get("sc_prob", None)
+    c.sc_id = kw.get("sc_id", None)
+    c.sc_status = kw.get("sc_status", None)
     return c
 
 
@@ -153,6 +158,41 @@ def test_invalid_step_block_and_pointers_are_refused(lib):
 def test_invalid_tail_is_refused(lib, kw):
     assert _step(lib, _ctx(**kw)) == dgd.DGD_EINVAL
     assert dgd.dgd_last_error()
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(sc_topk=-1, vocab_layout=1, sc_prob=FAKE, sc_id=FAKE), dgd.DGD_EINVAL),
+    (dict(sc_topk=33, vocab_layout=1, sc_prob=FAKE, sc_id=FAKE), dgd.DGD_EINVAL),
+    (dict(sc_topk=8, V=7, vocab_layout=1, sc_prob=FAKE, sc_id=FAKE), dgd.DGD_EINVAL),   # K > V
+    (dict(sc_topk=8, vocab_layout=1, sc_id=FAKE), dgd.DGD_EINVAL),                   # no sc_prob
+    (dict(sc_topk=8, vocab_layout=1, sc_prob=FAKE), dgd.DGD_EINVAL),                 # no sc_id
+    (dict(sc_topk=8, vocab_layout=0, sc_prob=FAKE, sc_id=FAKE), dgd.DGD_EUNSUPPORTED),  # rows
+])
+def test_invalid_self_conditioning_is_refused(lib, kw, code):
+    assert _step(lib, _ctx(**kw)) == code
+    assert dgd.dgd_last_error()
+
+
+def test_sc_embed_refusals(lib):
+    f = lib.dgd_sc_embed
+    ok = (FAKE, FAKE, 4, 8, FAKE, 1, 1024, 64, 8.0, FAKE, None)
+
+    def call(**kw):
+        names = ["prob", "ids", "rows", "K", "W", "layout", "V", "d", "scale", "out", "stream"]
+        args = dict(zip(names, ok))
+        args.update(kw)
+        return f(*[args[n] for n in names])
+
+    assert call(rows=0) == dgd.DGD_OK                      # nothing to do, nothing read
+    for kw, code in [(dict(prob=None), dgd.DGD_EINVAL), (dict(ids=None), dgd.DGD_EINVAL),
+                     (dict(W=None), dgd.DGD_EINVAL), (dict(out=None), dgd.DGD_EINVAL),
+                     (dict(rows=-1), dgd.DGD_EINVAL), (dict(K=0), dgd.DGD_EINVAL),
+                     (dict(K=33), dgd.DGD_EINVAL), (dict(V=0), dgd.DGD_EUNSUPPORTED),
+                     (dict(d=60), dgd.DGD_EUNSUPPORTED), (dict(layout=2), dgd.DGD_EINVAL),
+                     (dict(scale=float("nan")), dgd.DGD_EINVAL),
+                     (dict(W=FAKE + 4), dgd.DGD_EINVAL), (dict(out=FAKE + 2), dgd.DGD_EINVAL)]:
+        assert call(**kw) == code, kw
+        assert dgd.dgd_last_error()
 
 
 def test_tail_overlap_is_checked_over_every_step_of_a_run(lib):

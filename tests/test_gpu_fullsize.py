@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 from oracle import dgd_oracle as O
-from tests.parity import Report, compare_stats
+from tests.parity import Report, compare_sc, compare_stats
 from uniform_state_discrete_step_amd.inputs import WORKLOADS, make_workload_arrays, shrink
 
 pytestmark = pytest.mark.gpu
@@ -35,7 +35,8 @@ def dev():
 class FullRun:
     """Step a workload on the GPU with dgd_step and check every step."""
 
-    def __init__(self, wl, dev, W=None, Hs=None, layout=1, Wd=None, tail: O.Tail = None):
+    def __init__(self, wl, dev, W=None, Hs=None, layout=1, Wd=None, tail: O.Tail = None,
+                 sc_topk=0):
         import torch
         from uniform_state_discrete_step_amd import dgd
         self.torch, self.dgd, self.wl, self.dev = torch, dgd, wl, dev
@@ -55,8 +56,10 @@ class FullRun:
                 tkw["norm_weight"] = torch.from_numpy(tail.norm_weight.view(np.int16)).to(dev)
                 tkw["norm_eps"] = tail.norm_eps
             tkw["softcap"] = tail.softcap
+        self.sc_topk = sc_topk
         self.ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev,
-                               vocab_layout=layout, **tkw)
+                               vocab_layout=layout, sc_topk=sc_topk, sc_status=sc_topk > 0,
+                               **tkw)
         self.params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence,
                                       wl.stability_threshold, wl.freeze, wl.final_emit)
         self.P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,
@@ -86,6 +89,12 @@ class FullRun:
             z = O.logits(self.Hs[b, s, c][rows], self.W, self.tail, W64=self.W64)
             st = O.position_stats(z, T, wl.seeds[c], b * wl.L + rows, b * wl.N + s)
             sl = slice(c * wl.L, (c + 1) * wl.L)
+            if self.sc_topk:
+                K = self.sc_topk
+                compare_sc(rep, f"block {b} step {s} canvas {c}", z, T, K,
+                           self.ctx.sc_prob.cpu().numpy().reshape(-1, K)[sl][rows],
+                           self.ctx.sc_id.cpu().numpy().reshape(-1, K)[sl][rows],
+                           self.ctx.sc_status.cpu().numpy()[sl][rows], rows=rows)
             compare_stats(rep, f"block {b} step {s} canvas {c} rows {rows.tolist()}", st,
                           self.ctx.entropy[sl].cpu().numpy()[rows],
                           self.ctx.argmax[sl].cpu().numpy().astype(np.int64)[rows],
@@ -173,6 +182,19 @@ def test_gemma_vocab_full_run_with_lm_head_tail(dev):
     tail = O.Tail(norm_weight=make_norm_weight(wl.d, wl.cfg_seed), norm_eps=1e-6, softcap=30.0)
     _check(FullRun(wl, dev, tail=tail).run(sample_every=6, rows_per_canvas=6),
            f"{wl.name} with output norm and softcap")
+
+
+def test_gemma_vocab_full_run_with_self_conditioning(dev):
+    """Top-32 per position at the full size, with the output norm and softcap."""
+    from uniform_state_discrete_step_amd.inputs import make_norm_weight
+    wl = WORKLOADS["gemma_vocab"]
+    tail = O.Tail(norm_weight=make_norm_weight(wl.d, wl.cfg_seed), norm_eps=1e-6, softcap=30.0)
+    run = FullRun(wl, dev, tail=tail, sc_topk=32)
+    rep = run.run(sample_every=8, rows_per_canvas=6)
+    st = run.ctx.sc_status.cpu().numpy()
+    print(f"\nrecomputed parts in the last step: {int(st.sum())}, rows budget-exhausted "
+          f"{int((st < 0).sum())}", flush=True)
+    _check(rep, f"{wl.name} with self-conditioning top-32")
 
 
 @pytest.mark.parametrize("layout", [1, 0], ids=["packed", "rows"])

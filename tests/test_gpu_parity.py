@@ -37,13 +37,14 @@ def bf16(x):
     return f32_to_bf16_bits(np.asarray(x, dtype=np.float32))
 
 
-def run_lockstep(wl, dev, W=None, Hs=None, logits=False, layout=0, tail=None, **kw):
+def run_lockstep(wl, dev, W=None, Hs=None, logits=False, layout=0, tail=None, sc_topk=0, **kw):
     if W is None:
         W, Hs = make_workload_arrays(wl, threads=8)
-    ls = Lockstep(wl, W, Hs, dev, logits=logits, layout=layout, tail=tail)
+    ls = Lockstep(wl, W, Hs, dev, logits=logits, layout=layout, tail=tail, sc_topk=sc_topk)
     rep = ls.run(**kw)
     tag = "" if tail is None else (f" norm={tail.norm_weight is not None} eps={tail.norm_eps}"
                                    f" softcap={tail.softcap}")
+    tag += f" sc_topk={sc_topk}" if sc_topk else ""
     print(f"\n[{wl.name} layout={layout} B={wl.B} L={wl.L} G={wl.G} V={wl.V} d={wl.d} N={wl.N} "
           f"freeze={wl.freeze} final_emit={wl.final_emit}{tag}] {rep.summary()}", flush=True)
     assert not rep.failures, "\n".join(rep.failures)
@@ -174,6 +175,104 @@ def test_tail_logits_are_the_projection_of_the_normalised_rows(dev, layout):
     z_gpu, z = _logit_check(wl, dev, W, Hs, steps=[0, 1], layout=layout, tail=tail)
     # ctx->logits holds the projection before the cap: some logits exceed it
     assert np.abs(z_gpu).max() > 6.0
+
+
+# ----------------------------------------------------------------------------
+# self-conditioning: top-K per position and the embedding sum
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("K", [32, 5, 1])
+def test_sc_topk_lockstep(dev, K):
+    run_lockstep(WORKLOADS["tiny"], dev, layout=1, sc_topk=K)
+
+
+@pytest.mark.parametrize("shape,K", [
+    (dict(V=1001, d=72, L=37, B=3, G=74, N=5), 32),
+    (dict(V=4096, d=136, L=70, B=2, G=70, N=4), 32),
+    (dict(V=129, d=8, L=1, B=2, G=3, N=4), 32),
+    (dict(V=40, d=64, L=16, B=1, G=16, N=3), 32),      # lists cannot hold K: parts recomputed
+    (dict(V=1, d=16, L=5, B=1, G=5, N=3), 1),
+    (dict(V=70000, d=96, L=48, B=1, G=48, N=3), 32),   # 274 tiles: groups of 2 tiles
+], ids=["ragged", "straddle", "one_position", "v40", "v1", "two_tile_groups"])
+def test_sc_topk_ragged(dev, shape, K):
+    B = shape["B"]
+    wl = shrink(WORKLOADS["tiny"], name="ragged_sc", cfg_seed=13, seeds=tuple(range(B)),
+                bounds=tuple((0.1, 0.3, 0.05)[c % 3] for c in range(B)), **shape)
+    ls, rep = run_lockstep(wl, dev, layout=1, sc_topk=K)
+    if wl.V == 40:
+        assert rep.sc_recomputed > 0
+
+
+def test_sc_topk_with_tail_and_small_vocab(dev):
+    wl = WORKLOADS["small_vocab"]
+    run_lockstep(wl, dev, layout=1, tail=_tail(wl, softcap=30.0), sc_topk=32,
+                 steps=range(0, 48, 12))
+
+
+def _clustered_table(wl, seed=21):
+    """A table whose highest logits for every position sit together: rows
+    0..39 (one band of tile 0) and rows 256+{0,1,2,3,8} (one lane's ids in
+    tile 1) copy a row aligned with every position's hidden state, so the
+    band list and a lane list both overflow and must be recomputed."""
+    W, Hs = make_workload_arrays(wl, threads=1)
+    W = W.copy()
+    Hf = O.bf16_to_f64(Hs).reshape(-1, wl.d)
+    u = Hf.sum(axis=0)
+    u /= np.linalg.norm(u)
+    rng = np.random.default_rng(seed)
+    for v in range(40):
+        W[v] = bf16(u * 8.0 + rng.standard_normal(wl.d) * 1e-2)
+    for v in (256, 257, 258, 259, 264):
+        W[v] = bf16(u * 8.0 + rng.standard_normal(wl.d) * 1e-2)
+    return W, Hs, u
+
+
+def test_sc_topk_recomputes_overflowing_lists(dev):
+    wl = shrink(WORKLOADS["tiny"], name="clustered", L=16, G=16, N=4,
+                scale=(5.0, 10.0))
+    W, Hs, _ = _clustered_table(wl)
+    ls, rep = run_lockstep(wl, dev, W=W, Hs=Hs, layout=1, sc_topk=32)
+    assert rep.sc_recomputed > 0
+
+
+def test_sc_topk_exact_ties(dev):
+    """Identical table rows give identical logits: the lower id goes first.
+    Six copies of one dominant row lead every position's top K."""
+    wl = shrink(WORKLOADS["tiny"], name="ties", N=3, scale=(5.0, 10.0))
+    W, Hs, u = _clustered_table(wl)
+    W = make_workload_arrays(wl, threads=1)[0].copy()
+    for v in (3, 70, 300, 301, 500, 900):
+        W[v] = bf16(u * 8.0)
+    run_lockstep(wl, dev, W=W, Hs=Hs, layout=1, sc_topk=32)
+
+
+@pytest.mark.parametrize("layout", [0, 1], ids=["rows", "packed"])
+def test_sc_embed_matches_the_oracle(dev, layout):
+    import torch
+    from uniform_state_discrete_step_amd import dgd
+    wl = shrink(WORKLOADS["tiny"], V=3000, d=200, L=48, B=2, G=48, N=2, seeds=(4, 5),
+                bounds=(0.1, 0.2))
+    W, Hs = make_workload_arrays(wl, threads=1)
+    K = 32
+    ls = Lockstep(wl, W, Hs, dev, layout=1, sc_topk=K)
+    ls.run(steps=[0])
+    torch.cuda.synchronize()
+    rows = wl.B * wl.L
+    Wt = torch.from_numpy(W.view(np.int16)).to(dev)
+    if layout == 1:
+        Wt = dgd.pack_vocab(Wt, wl.V, wl.d)
+    out = torch.empty(rows * wl.d, dtype=torch.int16, device=dev)
+    scale = math.sqrt(wl.d)
+    dgd.dgd_sc_embed(ls.ctx.sc_prob, ls.ctx.sc_id, rows, K, Wt, layout, wl.V, wl.d, scale, out)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy().view(np.uint16).reshape(rows, wl.d)
+    p = ls.ctx.sc_prob.cpu().numpy().reshape(rows, K).astype(np.float64)
+    ids = ls.ctx.sc_id.cpu().numpy().reshape(rows, K)
+    o = O.sc_embed(p, ids, W, scale)
+    from tests.parity import ordered_bf16
+    ulp = np.abs(ordered_bf16(g) - ordered_bf16(o))
+    print(f"\n[sc_embed layout={layout}] max bf16 steps {ulp.max()}, "
+          f"inexact {np.count_nonzero(ulp)} of {ulp.size}", flush=True)
+    assert ulp.max() <= 1
 
 
 # ----------------------------------------------------------------------------

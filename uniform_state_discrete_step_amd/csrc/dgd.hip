@@ -73,12 +73,15 @@ struct ProjArgs {
   int32_t block, gstep;
   float c2;               // log2(e) / T_s
   float cap_in, cap_out;  // softcap: 1 / c and c * c2 (used only when the cap is on)
+  struct ScEnt* cand;     // [M][P][kScCand] self-conditioning candidates, or null
   uint32_t key[DGD_MAX_CANVASES][2];
 };
 
 struct CommitArgs {
   const Rec* part;
   int32_t P;
+  float* rowM;            // merged max (bits) and sum 2^(x2 - m) of each position
+  float* rowS;
   float* rowH;
   int32_t* rowA;
   int32_t* rowTok;
@@ -251,6 +254,99 @@ __device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int ha
   loc.y1 = y1; loc.i1 = i1; loc.y2 = y2; loc.pad = 0.f;
   const Rec oth = rec_shfl_xor(loc, 32);
   return rec_merge(rec_pick(half == 0, loc, oth), rec_pick(half == 0, oth, loc));
+}
+
+// ---------------------------------------------------------------------------
+// Self-conditioning top-K: candidate lists built in the projection's epilogue
+// ---------------------------------------------------------------------------
+// For every position and every vocabulary band of its group (the 64 rows of
+// each of the group's tiles that one wave owns), the epilogue keeps a list of
+// the kScWave largest tempered logits seen over the group's tiles, with their
+// ids.  Each lane first takes the top kScLane values of its own 32 ids in the
+// tile; the two lanes of a position then merge theirs into the band list in
+// LDS.  Lists order by value only (equal values in any order): every value a
+// list dropped is at most its last entry, which is tagged.  k_sc_topk
+// recomputes a list's part of the vocabulary exactly whenever a tagged value
+// reaches the K-th selected value, so its result is exact, ties included.
+constexpr int kScLane = 3;                     // per-lane list: one tile, 32 ids
+constexpr int kScWave = 4;                     // per-(band, position) list over the tiles
+constexpr int kScCand = kVGroups * kScWave;    // candidates per (position, group)
+constexpr uint32_t kScLaneTag = 0x80000000u;   // last entry of a lane list
+constexpr uint32_t kScWaveTag = 0x40000000u;   // last entry of a band list
+constexpr uint32_t kScIdBits = 0x3FFFFFFFu;
+constexpr uint32_t kScNoId = kScIdBits;        // empty slot: never a valid id
+
+struct ScEnt {
+  float x;       // tempered logit in bits (x2 = z * log2(e) / T, or the capped value)
+  uint32_t id;   // vocabulary id | tags
+};
+static_assert(sizeof(ScEnt) == 8, "candidate is 8 bytes");
+
+// Insert (x, i) into a list sorted by value, largest first, dropping its last
+// entry (an equal value goes after the entries already there).
+template <int N>
+__device__ __forceinline__ void sc_insert(float (&lx)[N], uint32_t (&li)[N], float x, uint32_t i) {
+  bool b[N];
+#pragma unroll
+  for (int k = 0; k < N; ++k) b[k] = x > lx[k];
+#pragma unroll
+  for (int k = N - 1; k >= 1; --k) {
+    lx[k] = b[k - 1] ? lx[k - 1] : (b[k] ? x : lx[k]);
+    li[k] = b[k - 1] ? li[k - 1] : (b[k] ? i : li[k]);
+  }
+  lx[0] = b[0] ? x : lx[0];
+  li[0] = b[0] ? i : li[0];
+}
+
+__device__ __forceinline__ void sc_list_clear(ScEnt* slot) {
+  const u32x4_t e = {__float_as_uint(kNeg), kScNoId, __float_as_uint(kNeg), kScNoId};
+  reinterpret_cast<u32x4_t*>(slot)[0] = e;
+  reinterpret_cast<u32x4_t*>(slot)[1] = e;
+}
+
+// One tile of one position: z holds the lane's 32 tempered logits (after
+// tile_record, ids past V already masked); slot is the position's band list
+// in LDS, updated by the lane of half 0.
+__device__ __forceinline__ void sc_tile_update(const f32x16_t (&z)[kVB], int vbase, int half,
+                                               ScEnt* slot) {
+  // top kScLane values of the lane's 32 ids, by sorted insertion
+  static_assert(kScLane == 3 && kScWave == 4, "list sizes");
+  float t0 = -INFINITY, t1 = -INFINITY, t2 = -INFINITY;
+  int o0 = 0, o1 = 0, o2 = 0;
+#pragma unroll
+  for (int i = 0; i < kVB * 16; ++i) {
+    const float x = z[i >> 4][i & 15];
+    const int off = (i >> 4) * 32 + 8 * ((i >> 2) & 3) + (i & 3);
+    const bool c0 = x > t0, c1 = x > t1, c2 = x > t2;
+    t2 = c1 ? t1 : (c2 ? x : t2);
+    o2 = c1 ? o1 : (c2 ? off : o2);
+    t1 = c0 ? t0 : (c1 ? x : t1);
+    o1 = c0 ? o0 : (c1 ? off : o1);
+    t0 = c0 ? x : t0;
+    o0 = c0 ? off : o0;
+    if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+  }
+  const uint32_t base = (uint32_t)(vbase + 4 * half);
+  const uint32_t i0 = base + o0, i1 = base + o1, i2 = (base + o2) | kScLaneTag;
+  const float u0 = __shfl_xor(t0, 32), u1 = __shfl_xor(t1, 32), u2 = __shfl_xor(t2, 32);
+  const uint32_t j0 = __shfl_xor(i0, 32), j1 = __shfl_xor(i1, 32), j2 = __shfl_xor(i2, 32);
+  if (half == 0) {
+    const u32x4_t a = reinterpret_cast<const u32x4_t*>(slot)[0];
+    const u32x4_t b = reinterpret_cast<const u32x4_t*>(slot)[1];
+    float lx[kScWave] = {__uint_as_float(a[0]), __uint_as_float(a[2]), __uint_as_float(b[0]),
+                         __uint_as_float(b[2])};
+    uint32_t li[kScWave] = {a[1], a[3], b[1], b[3]};
+    sc_insert(lx, li, t0, i0);
+    sc_insert(lx, li, t1, i1);
+    sc_insert(lx, li, t2, i2);
+    sc_insert(lx, li, u0, j0);
+    sc_insert(lx, li, u1, j1);
+    sc_insert(lx, li, u2, j2);
+    const u32x4_t na = {__float_as_uint(lx[0]), li[0], __float_as_uint(lx[1]), li[1]};
+    const u32x4_t nb = {__float_as_uint(lx[2]), li[2], __float_as_uint(lx[3]), li[3]};
+    reinterpret_cast<u32x4_t*>(slot)[0] = na;
+    reinterpret_cast<u32x4_t*>(slot)[1] = nb;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -550,7 +646,7 @@ __global__ void __launch_bounds__(kThreads) k_pack_vocab(const uint16_t* __restr
 //   * one barrier per chunk, inside MFMA step 3 (see chunk()).
 // The H stream is cyclic over the chunks, so a tile finds the first HB chunks
 // of H already in LDS.
-template <int NB, bool kLogits, bool kUniformKey, bool kCap, int PW, int RING, int HB>
+template <int NB, bool kLogits, bool kUniformKey, bool kCap, bool kTopK, int PW, int RING, int HB>
 __global__ void __launch_bounds__(256 * PW) __attribute__((amdgpu_waves_per_eu(PW, PW)))
 k_project_packed(const ProjArgs a) {
   static_assert(NB == 1 || NB == 2 || NB == 4 || NB == 8, "NB");
@@ -573,6 +669,8 @@ k_project_packed(const ProjArgs a) {
   static_assert(kDmaLag <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t hsm[HB][HBUF];
   __shared__ __attribute__((aligned(16))) Rec recs[WAVES * PPW];
+  // self-conditioning band lists, kScWave entries per (wave, position)
+  __shared__ __attribute__((aligned(16))) ScEnt slist[kTopK ? WAVES * PPW * kScWave : 1];
 
   const int tid = threadIdx.x;
   // wave indices are uniform: keep them (and the buffer resources built from
@@ -591,6 +689,8 @@ k_project_packed(const ProjArgs a) {
     if (all_done) return;
   }
   for (int i = tid; i < WAVES * PPW; i += THREADS) rec_store(recs + i, rec_empty());
+  if constexpr (kTopK)
+    for (int i = tid; i < WAVES * PPW; i += THREADS) sc_list_clear(slist + i * kScWave);
 
   const int nk = packed_chunks(a.d);
   const int nkr = (nk + RING - 1) / RING * RING;   // chunk loop padded to whole rings
@@ -789,6 +889,7 @@ k_project_packed(const ProjArgs a) {
         Rec* slot = recs + wave * PPW + pb * 32 + col;
         rec_store(slot, rec_merge(rec_load(slot), wrec));
       }
+      if constexpr (kTopK) sc_tile_update(z, vbase, half, slist + (wave * PPW + pb * 32 + col) * kScWave);
 #pragma unroll
       for (int vb = 0; vb < kVB; ++vb)
 #pragma unroll
@@ -805,6 +906,17 @@ k_project_packed(const ProjArgs a) {
     for (int w = 1; w < 4; ++w) r = rec_merge(r, rec_load(recs + (tp * 4 + w) * PPW + lp));
     const int row = row0 + t;
     if (row < a.M) rec_store(a.part + (size_t)row * a.P + g, r);
+  }
+  // ------- self-conditioning candidates: the four band lists of each position -------
+  if constexpr (kTopK) {
+    for (int t = tid; t < MROWS * kScCand; t += THREADS) {
+      const int pos = t / kScCand, k = t % kScCand, band = k / kScWave, e = k % kScWave;
+      const int w = (pos / PPW) * 4 + band;
+      ScEnt ent = slist[(w * PPW + pos % PPW) * kScWave + e];
+      if (e == kScWave - 1) ent.id |= kScWaveTag;
+      const int row = row0 + pos;
+      if (row < a.M) a.cand[((size_t)row * a.P + g) * kScCand + k] = ent;
+    }
   }
 }
 
@@ -1073,6 +1185,8 @@ __global__ void __launch_bounds__(kThreads) k_merge(const CommitArgs a) {
     if (!(Hn > 0.0)) Hn = 0.0;
     const float H = (float)Hn;
     const float gap = (float)(((double)rec.y1 - (double)rec.y2) * kLn2);
+    a.rowM[r] = rec.m;
+    a.rowS[r] = rec.S;
     a.rowH[r] = H;
     a.rowA[r] = rec.am;
     a.rowTok[r] = rec.i1;
@@ -1080,6 +1194,277 @@ __global__ void __launch_bounds__(kThreads) k_merge(const CommitArgs a) {
     if (a.out_argmax) a.out_argmax[r] = rec.am;
     if (a.out_token) a.out_token[r] = rec.i1;
     if (a.out_gap) a.out_gap[r] = gap;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_sc_topk: the K most probable tokens of each position
+// ---------------------------------------------------------------------------
+// One workgroup per position.  The candidate pool starts as the position's
+// band lists of every group; keys order candidates by (logit desc, id asc):
+//   key = ord(x) << 32 | (0xFFFFFF - id) << 8 | tags,   0 = no candidate.
+// Selection: the K-th largest of the per-thread maxima bounds the K-th key
+// from below; the keys above that bound (at most 32 K) are sorted in LDS.
+// While a tagged candidate's value reaches the K-th selected value, the part
+// of the vocabulary its list covered (the lane's 32 ids in one tile, or the
+// whole band of the group) is recomputed exactly with fp32 dot products, its
+// old candidates leave the pool, the recomputed ones join it, and the
+// selection runs again.
+constexpr int kScMaxK = DGD_SC_MAX_TOPK;
+constexpr int kScPoolExtra = 4096;          // recomputed candidates per position
+constexpr int kScSortMax = 32 * kScMaxK;    // keys above the bound
+
+struct ScArgs {
+  const ScEnt* cand;      // [M][P][kScCand]
+  const float* rowM;
+  const float* rowS;
+  const uint16_t* H;      // rows the projection read
+  const uint16_t* W;      // packed table
+  const int32_t* done;
+  float* out_prob;        // [M][K]
+  int32_t* out_id;        // [M][K]
+  int32_t* out_status;    // [M] or null
+  int32_t M, V, d, L, P, K, n_vtiles;
+  float c2, cap_in, cap_out;
+  int32_t cap;
+};
+
+__device__ __forceinline__ uint64_t sc_key(float x, uint32_t idtag) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t id = idtag & kScIdBits;
+  return ((uint64_t)ord << 32) | ((uint64_t)(0xFFFFFFu - id) << 8) | (idtag >> 30);
+}
+__device__ __forceinline__ float sc_key_x(uint64_t k) {
+  const uint32_t ord = (uint32_t)(k >> 32);
+  return __uint_as_float((ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord);
+}
+__device__ __forceinline__ uint32_t sc_key_id(uint64_t k) {
+  return 0xFFFFFFu - (uint32_t)((k >> 8) & 0xFFFFFFu);
+}
+
+// Descending bitonic sort of buf[0..n), n a power of two <= 2 * kThreads * 8.
+__device__ void sc_sort_desc(uint64_t* buf, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += kThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = buf[i], y = buf[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            buf[i] = y;
+            buf[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Tempered logit of vocabulary id v for one position, recomputed from the
+// packed table: an fp32 dot product in hidden order, then the same
+// temperature (or softcap) transform as the projection's epilogue.
+__device__ float sc_logit(const ScArgs& a, const uint16_t* hrow, int v) {
+  const int nk = packed_chunks(a.d);
+  const int rg = v / kPackRows, f = (v % kPackRows) / 32, lv = v % 32;
+  float acc = 0.f;
+  for (int c = 0; c < nk; ++c) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const int k0 = c * kKChunk + 32 * h + 8 * s;
+        if (k0 >= a.d) continue;
+        const size_t u = ((((size_t)rg * nk + c) * 4 + s) * 2 + f) * 64 + lv + 32 * h;
+        const u32x4_t w = *(const u32x4_t*)(a.W + u * 8);
+        const u32x4_t x = *(const u32x4_t*)(hrow + k0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc = fmaf(__uint_as_float(x[j] << 16), __uint_as_float(w[j] << 16), acc);
+          acc = fmaf(__uint_as_float(x[j] & 0xffff0000u), __uint_as_float(w[j] & 0xffff0000u), acc);
+        }
+      }
+  }
+  return a.cap ? softcap_bits(acc, a.cap_in, a.cap_out) : __fmul_rn(acc, a.c2);
+}
+
+__global__ void __launch_bounds__(kThreads) k_sc_topk(const ScArgs a) {
+  __shared__ uint64_t pool[kMaxGroups * kScCand + kScPoolExtra];
+  __shared__ uint64_t sbuf[kScSortMax];
+  __shared__ uint64_t tmax[kThreads];
+  __shared__ int s_cnt;
+  __shared__ uint64_t s_tagged;
+  const int row = blockIdx.x;
+  if (a.done[row / a.L]) return;
+  const int tid = threadIdx.x;
+  const int n0 = a.P * kScCand;
+  {
+    // all loads first (independent), then the keys
+    constexpr int kPer = kMaxGroups * kScCand / kThreads;
+    ScEnt e[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < n0) e[j] = a.cand[(size_t)row * n0 + i];
+    }
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < n0) pool[i] = (e[j].id & kScIdBits) < (uint32_t)a.V ? sc_key(e[j].x, e[j].id) : 0ull;
+    }
+  }
+  int npool = n0;
+  int status = 0;
+  const uint16_t* hrow = a.H + (size_t)row * a.d;
+  __syncthreads();
+  for (;;) {
+    // ---- select: bound from the per-thread maxima, then sort what is above it
+    uint64_t mx = 0;
+    for (int i = tid; i < npool; i += kThreads) mx = max(mx, pool[i]);
+    tmax[tid] = mx;
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    sc_sort_desc(tmax, kThreads);
+    const uint64_t bound = tmax[a.K - 1];
+    for (int i = tid; i < npool; i += kThreads) {
+      const uint64_t k = pool[i];
+      if (k != 0 && k >= bound) sbuf[atomicAdd(&s_cnt, 1)] = k;
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    int n = 64;
+    while (n < cnt) n <<= 1;
+    for (int i = cnt + tid; i < n; i += kThreads) sbuf[i] = 0;
+    __syncthreads();
+    sc_sort_desc(sbuf, n);
+    // ---- a tagged candidate whose value reaches the K-th selected value:
+    // its list may have dropped values as large as its own (the largest such
+    // key is taken; none, and the selection is exact)
+    const uint64_t kth = sbuf[a.K - 1];
+    const uint32_t kth_ord = (uint32_t)(kth >> 32);     // 0 when fewer than K
+    if (tid == 0) s_tagged = 0;
+    __syncthreads();
+    {
+      uint64_t best = 0;
+      for (int i = tid; i < npool; i += kThreads) {
+        const uint64_t k = pool[i];
+        if ((k & 3ull) && (uint32_t)(k >> 32) >= kth_ord) best = max(best, k);
+      }
+      if (best) atomicMax((unsigned long long*)&s_tagged, (unsigned long long)best);
+    }
+    __syncthreads();
+    const uint64_t tagged = s_tagged;
+    if (tagged == 0) break;
+    // ---- recompute the part of the vocabulary the tagged list covered
+    const uint32_t tid_v = sc_key_id(tagged);
+    const int vt = (int)(tid_v / kVocabTile), band = (int)(tid_v % kVocabTile) / kVocabPerWave;
+    const int g = vt % a.P;
+    const bool whole_band = (tagged & 1ull) != 0;     // band list tag (id bit 30)
+    const int tiles = whole_band ? (a.n_vtiles - g + a.P - 1) / a.P : 1;
+    const int seg = whole_band ? tiles * kVocabPerWave : 32;
+    if (npool + seg > n0 + kScPoolExtra) { status = -1; break; }
+    // drop the part's candidates
+    const int half = (int)(tid_v % 8) / 4;
+    for (int i = tid; i < npool; i += kThreads) {
+      const uint64_t k = pool[i];
+      if (k == 0) continue;
+      const uint32_t v = sc_key_id(k);
+      const int kvt = (int)(v / kVocabTile), kband = (int)(v % kVocabTile) / kVocabPerWave;
+      const bool in = whole_band ? (kvt % a.P == g && kband == band)
+                                 : (kvt == vt && kband == band && (int)(v % 8) / 4 == half);
+      if (in) pool[i] = 0;
+    }
+    // recompute it: one id per thread
+    for (int i = tid; i < seg; i += kThreads) {
+      int v;
+      if (whole_band) {
+        v = (g + (i / kVocabPerWave) * a.P) * kVocabTile + band * kVocabPerWave + i % kVocabPerWave;
+      } else {
+        v = vt * kVocabTile + band * kVocabPerWave + (i / 16) * 32 + 8 * ((i / 4) % 4) + 4 * half + i % 4;
+      }
+      pool[npool + i] = v < a.V ? sc_key(sc_logit(a, hrow, v), (uint32_t)v) : 0ull;
+    }
+    npool += seg;
+    ++status;
+    __syncthreads();
+  }
+  // ---- outputs: probabilities 2^(x - m) / S, best first
+  if (tid < a.K) {
+    // (a key of 0 is left only when the recomputation budget ran out)
+    const uint64_t k = sbuf[tid];
+    const float p = k ? fexp2(sc_key_x(k) - a.rowM[row]) / a.rowS[row] : 0.f;
+    a.out_prob[(size_t)row * a.K + tid] = p;
+    a.out_id[(size_t)row * a.K + tid] = k ? (int32_t)sc_key_id(k) : -1;
+  }
+  if (tid == 0 && a.out_status) a.out_status[row] = status;
+}
+
+// ---------------------------------------------------------------------------
+// k_sc_embed: the self-conditioning input, scale * sum_j bf16(p_j) E[id_j]
+// ---------------------------------------------------------------------------
+// One workgroup per row.  The row's K (probability, id) pairs go to LDS
+// first; each thread then owns 8 consecutive hidden elements (16 bytes of
+// every table row) and adds the K scaled pieces in order, in fp32, with the
+// loads of 8 pieces in flight at a time, and rounds once to bf16 (nearest,
+// ties to even).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__global__ void __launch_bounds__(kThreads) k_sc_embed(const float* __restrict__ prob,
+                                                       const int32_t* __restrict__ ids, int K,
+                                                       const uint16_t* __restrict__ W, int packed,
+                                                       int V, int d, float scale,
+                                                       uint16_t* __restrict__ out) {
+  __shared__ float sp[kScMaxK];
+  __shared__ int32_t sid[kScMaxK];
+  const int row = blockIdx.x;
+  if (threadIdx.x < K) {
+    // bf16(p); ids outside [0, V) contribute nothing (weight 0, row 0)
+    const int v = ids[(size_t)row * K + threadIdx.x];
+    const bool ok = v >= 0 && v < V;
+    sp[threadIdx.x] = ok ? __uint_as_float(f32_to_bf16_rne(prob[(size_t)row * K + threadIdx.x]) << 16) : 0.f;
+    sid[threadIdx.x] = ok ? v : 0;
+  }
+  __syncthreads();
+  const int nk = packed_chunks(d);
+  for (int k0 = threadIdx.x * 8; k0 < d; k0 += kThreads * 8) {
+    const int c = k0 / kKChunk, h = (k0 % kKChunk) / 32, s = (k0 % 32) / 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < K; j0 += 8) {
+      u32x4_t w[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj < K ? j0 + jj : K - 1;
+        const int v = sid[j];
+        size_t off;
+        if (packed) {
+          const int rg = v / kPackRows, f = (v % kPackRows) / 32, lv = v % 32;
+          off = (((((size_t)rg * nk + c) * 4 + s) * 2 + f) * 64 + lv + 32 * h) * 8;
+        } else {
+          off = (size_t)v * d + k0;
+        }
+        w[jj] = *(const u32x4_t*)(W + off);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        if (j0 + jj >= K) break;
+        const float pj = sp[j0 + jj];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(pj, __uint_as_float(w[jj][e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(pj, __uint_as_float(w[jj][e] & 0xffff0000u), acc[2 * e + 1]);
+        }
+      }
+    }
+    u32x4_t r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      r[e] = f32_to_bf16_rne(acc[2 * e] * scale) | (f32_to_bf16_rne(acc[2 * e + 1] * scale) << 16);
+    *(u32x4_t*)(out + (size_t)row * d + k0) = r;
   }
 }
 
@@ -1141,7 +1526,7 @@ int hip_fail(hipError_t e, const char* what) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t part, rowH, rowA, rowTok, total;
+  size_t part, rowM, rowS, rowH, rowA, rowTok, cand, total;
   int P;
 };
 
@@ -1151,9 +1536,12 @@ WsLayout ws_layout(int B, int L, int V) {
   w.P = num_groups(V);
   size_t off = 0;
   w.part = off;     off = align256(off + M * (size_t)w.P * sizeof(Rec));
+  w.rowM = off;     off = align256(off + M * sizeof(float));
+  w.rowS = off;     off = align256(off + M * sizeof(float));
   w.rowH = off;     off = align256(off + M * sizeof(float));
   w.rowA = off;     off = align256(off + M * sizeof(int32_t));
   w.rowTok = off;   off = align256(off + M * sizeof(int32_t));
+  w.cand = off;     off = align256(off + M * (size_t)w.P * kScCand * sizeof(ScEnt));
   w.total = off;
   return w;
 }
@@ -1202,6 +1590,18 @@ int check_shape(const dgd_ctx* ctx) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// The optional self-conditioning outputs.
+int check_sc(const dgd_ctx* ctx) {
+  const int K = ctx->sc_topk;
+  if (K == 0) return DGD_OK;
+  if (K < 0 || K > DGD_SC_MAX_TOPK) return fail(DGD_EINVAL, "sc_topk=%d outside [0, %d]", K, DGD_SC_MAX_TOPK);
+  if (K > ctx->V) return fail(DGD_EINVAL, "sc_topk=%d exceeds V=%d", K, ctx->V);
+  if (ctx->vocab_layout != DGD_VOCAB_PACKED)
+    return fail(DGD_EUNSUPPORTED, "sc_topk needs the packed vocabulary layout");
+  if (!ctx->sc_prob || !ctx->sc_id) return fail(DGD_EINVAL, "sc_topk is set but sc_prob/sc_id is NULL");
+  return DGD_OK;
+}
 
 // The optional lm-head tail; H_bytes is the extent of H (all steps for dgd_run).
 int check_tail(const dgd_ctx* ctx, const void* H, size_t H_bytes) {
@@ -1329,7 +1729,7 @@ void with_flags(F&& f, bool b, Rest... rest) {
 }
 
 struct Flags {
-  bool logits, uniform, cap;
+  bool logits, uniform, cap, topk;
 };
 
 template <int MB>
@@ -1350,11 +1750,11 @@ constexpr int kPackedPW = 1, kPackedRing = 2, kPackedHB = 2;
 template <int NB>
 void launch_packed_nb(const ProjArgs& a, dim3 grid, hipStream_t s, Flags fl) {
   constexpr int PW = kPackedPW, R = kPackedRing, HB = kPackedHB;
-  with_flags([&](auto lg, auto uni, auto cap) {
+  with_flags([&](auto lg, auto uni, auto cap, auto topk) {
     hipLaunchKernelGGL((k_project_packed<NB, decltype(lg)::value, decltype(uni)::value,
-                                         decltype(cap)::value, PW, R, HB>),
+                                         decltype(cap)::value, decltype(topk)::value, PW, R, HB>),
                        grid, dim3(256 * PW), 0, s, a);
-  }, fl.logits, fl.uniform, fl.cap);
+  }, fl.logits, fl.uniform, fl.cap, fl.topk);
 }
 
 int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* committed,
@@ -1394,7 +1794,9 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
     pa.cap_out = (float)(ctx->softcap * kLog2e / T);
   }
   fill_keys(pa.key, seed, B);
-  const Flags fl{ctx->logits != nullptr, (L % 32) == 0, cap};
+  const bool topk = ctx->sc_topk > 0;
+  if (topk) pa.cand = (ScEnt*)(ws + wl.cand);
+  const Flags fl{ctx->logits != nullptr, (L % 32) == 0, cap, topk};
   int rc;
   if (ctx->vocab_layout == DGD_VOCAB_PACKED) {
     const int NB = M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8;
@@ -1425,6 +1827,8 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
 
   CommitArgs ca{};
   ca.part = pa.part; ca.P = wl.P;
+  ca.rowM = (float*)(ws + wl.rowM);
+  ca.rowS = (float*)(ws + wl.rowS);
   ca.rowH = (float*)(ws + wl.rowH);
   ca.rowA = (int32_t*)(ws + wl.rowA);
   ca.rowTok = (int32_t*)(ws + wl.rowTok);
@@ -1444,6 +1848,19 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   hipLaunchKernelGGL(k_merge, grid2, dim3(kThreads), 0, stream, ca);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "k_merge launch");
+  if (topk) {
+    // before k_commit: a canvas this step finishes still gets its distribution
+    ScArgs sa{};
+    sa.cand = pa.cand; sa.rowM = ca.rowM; sa.rowS = ca.rowS;
+    sa.H = pa.H; sa.W = pa.W; sa.done = sv.done;
+    sa.out_prob = ctx->sc_prob; sa.out_id = ctx->sc_id; sa.out_status = ctx->sc_status;
+    sa.M = M; sa.V = V; sa.d = dd; sa.L = L; sa.P = wl.P; sa.K = ctx->sc_topk;
+    sa.n_vtiles = pa.n_vtiles;
+    sa.c2 = pa.c2; sa.cap_in = pa.cap_in; sa.cap_out = pa.cap_out; sa.cap = cap ? 1 : 0;
+    hipLaunchKernelGGL(k_sc_topk, dim3(M), dim3(kThreads), 0, stream, sa);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "k_sc_topk launch");
+  }
   hipLaunchKernelGGL(k_commit, dim3(B), dim3(kThreads), 0, stream, ca);
   e = hipGetLastError();
   return e == hipSuccess ? DGD_OK : hip_fail(e, "k_commit launch");
@@ -1495,6 +1912,7 @@ int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_
   if (!H || !W_vocab || !canvas || !committed) return fail(DGD_EINVAL, "H/W_vocab/canvas/committed is NULL");
   if (!aligned16(H) || !aligned16(W_vocab)) return fail(DGD_EINVAL, "H/W_vocab is not 16-byte aligned");
   if ((rc = check_tail(ctx, H, (size_t)ctx->B * ctx->L * ctx->d * 2))) return rc;
+  if ((rc = check_sc(ctx))) return rc;
   if (block < 0 || block >= ctx->G / ctx->L)
     return fail(DGD_EINVAL, "block=%d outside [0, %d)", block, ctx->G / ctx->L);
   if (step < 0 || step >= params->num_inference_steps)
@@ -1522,6 +1940,7 @@ int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas, u
   const int blocks = ctx->G / ctx->L;
   const size_t step_elems = (size_t)ctx->B * ctx->L * ctx->d;
   if ((rc = check_tail(ctx, H_steps, (size_t)blocks * N * step_elems * 2))) return rc;
+  if ((rc = check_sc(ctx))) return rc;
   Timer timer;
   timer.on = ctx->k1_ms != nullptr;
   for (int b = 0; b < blocks && rc == DGD_OK; ++b) {
@@ -1557,6 +1976,27 @@ int dgd_pack_vocab(const dgd_bf16* W_vocab, dgd_bf16* W_packed, int32_t V, int32
                      W_vocab, W_packed, V, d, packed_chunks(d), units);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? DGD_OK : hip_fail(e, "k_pack_vocab launch");
+}
+
+int dgd_sc_embed(const float* sc_prob, const int32_t* sc_id, int32_t rows, int32_t K,
+                 const dgd_bf16* W_vocab, int32_t vocab_layout, int32_t V, int32_t d, float scale,
+                 dgd_bf16* out, void* stream) {
+  g_err.clear();
+  if (!sc_prob || !sc_id || !W_vocab || !out) return fail(DGD_EINVAL, "sc_prob/sc_id/W_vocab/out is NULL");
+  if (rows < 0) return fail(DGD_EINVAL, "rows=%d < 0", rows);
+  if (K < 1 || K > DGD_SC_MAX_TOPK) return fail(DGD_EINVAL, "K=%d outside [1, %d]", K, DGD_SC_MAX_TOPK);
+  if (V < 1 || V > DGD_MAX_VOCAB) return fail(DGD_EUNSUPPORTED, "V=%d outside [1, 2^24]", V);
+  if (d < 8 || d > DGD_MAX_HIDDEN || d % 8 != 0)
+    return fail(DGD_EUNSUPPORTED, "d=%d must be a multiple of 8 in [8, %d]", d, DGD_MAX_HIDDEN);
+  if (vocab_layout != DGD_VOCAB_ROWS && vocab_layout != DGD_VOCAB_PACKED)
+    return fail(DGD_EINVAL, "vocab_layout=%d is neither DGD_VOCAB_ROWS nor DGD_VOCAB_PACKED", vocab_layout);
+  if (!std::isfinite(scale)) return fail(DGD_EINVAL, "scale is not finite");
+  if (!aligned16(W_vocab) || !aligned16(out)) return fail(DGD_EINVAL, "W_vocab/out is not 16-byte aligned");
+  if (rows == 0) return DGD_OK;
+  hipLaunchKernelGGL(k_sc_embed, dim3((unsigned)rows), dim3(kThreads), 0, (hipStream_t)stream, sc_prob, sc_id, K,
+                     W_vocab, vocab_layout == DGD_VOCAB_PACKED ? 1 : 0, V, d, scale, out);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_sc_embed launch");
 }
 
 int dgd_debug_gumbel(const uint32_t* words, float* out, int64_t n, void* stream) {

@@ -27,7 +27,8 @@ DGD_VOCAB_ROWS = 0
 DGD_VOCAB_PACKED = 1
 
 EXPORTED = ("dgd_state_bytes", "dgd_workspace_bytes", "dgd_init_block", "dgd_step", "dgd_run",
-            "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_debug_gumbel", "dgd_last_error")
+            "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_sc_embed", "dgd_debug_gumbel",
+            "dgd_last_error")
 
 
 class DgdError(RuntimeError):
@@ -70,6 +71,10 @@ class DgdCtx(ctypes.Structure):
         ("norm_eps", ctypes.c_float),
         ("softcap", ctypes.c_float),
         ("norm_h", ctypes.c_void_p),
+        ("sc_topk", ctypes.c_int32),
+        ("sc_prob", ctypes.c_void_p),
+        ("sc_id", ctypes.c_void_p),
+        ("sc_status", ctypes.c_void_p),
     ]
 
 
@@ -106,6 +111,10 @@ def load_library(path: str = LIB_PATH):
     lib.dgd_pack_vocab.restype = ctypes.c_int
     lib.dgd_pack_vocab.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_void_p]
+    lib.dgd_sc_embed.restype = ctypes.c_int
+    lib.dgd_sc_embed.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                 ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
     lib.dgd_debug_gumbel.restype = ctypes.c_int
     lib.dgd_debug_gumbel.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                      ctypes.c_void_p]
@@ -156,10 +165,12 @@ class Context:
 
     def __init__(self, B, L, V, d, G, bounds, device="cuda", outputs=True, logits=False,
                  commit_trace=False, vocab_layout=DGD_VOCAB_ROWS, norm_weight=None,
-                 norm_eps=0.0, softcap=0.0):
+                 norm_eps=0.0, softcap=0.0, sc_topk=0, sc_status=False):
         """norm_weight: optional device int16[d] (bf16 bits) output-norm weights;
         when given, ``norm_h`` (int16[B*L*d]) receives the normalised rows each
-        step.  softcap: the logit cap c (0 = none)."""
+        step.  softcap: the logit cap c (0 = none).  sc_topk: K > 0 allocates
+        ``sc_prob`` (float32[B*L*K]) and ``sc_id`` (int32[B*L*K]), and with
+        sc_status ``sc_status`` (int32[B*L])."""
         import torch
         lib = load_library()
         self.B, self.L, self.V, self.d, self.G = int(B), int(L), int(V), int(d), int(G)
@@ -191,6 +202,12 @@ class Context:
         self.softcap = float(softcap)
         self.norm_h = (torch.empty(BL * self.d, dtype=torch.int16, device=device)
                        if norm_weight is not None else None)
+        self.sc_topk = int(sc_topk)
+        K = max(self.sc_topk, 0)
+        self.sc_prob = torch.zeros(BL * K, dtype=torch.float32, device=device) if K else None
+        self.sc_id = torch.zeros(BL * K, dtype=torch.int32, device=device) if K else None
+        self.sc_status = (torch.zeros(BL, dtype=torch.int32, device=device)
+                          if K and sc_status else None)
 
     def state_views(self) -> dict:
         B, BL = self.B, self.B * self.L
@@ -229,6 +246,10 @@ class Context:
         c.norm_eps = self.norm_eps
         c.softcap = self.softcap
         c.norm_h = _ptr(self.norm_h)
+        c.sc_topk = self.sc_topk
+        c.sc_prob = _ptr(self.sc_prob)
+        c.sc_id = _ptr(self.sc_id)
+        c.sc_status = _ptr(self.sc_status)
         if self.time_k1:
             c.k1_ms = ctypes.pointer(self._k1_ms)
             c.k1_launches = ctypes.pointer(self._k1_n)
@@ -287,6 +308,13 @@ def pack_vocab(W_vocab, V: int, d: int, stream=None):
     out = torch.empty(dgd_packed_vocab_bytes(V, d) // 2, dtype=torch.int16, device=W_vocab.device)
     dgd_pack_vocab(W_vocab, out, V, d, stream)
     return out
+
+
+def dgd_sc_embed(sc_prob, sc_id, rows: int, K: int, W_vocab, vocab_layout: int, V: int, d: int,
+                 scale: float, out, stream=None):
+    _check(load_library().dgd_sc_embed(_ptr(sc_prob, 4), _ptr(sc_id, 4), int(rows), int(K),
+                                       _ptr(W_vocab, 2), int(vocab_layout), int(V), int(d),
+                                       float(scale), _ptr(out, 2), _stream_handle(stream)))
 
 
 def dgd_debug_gumbel(words, out, stream=None):
