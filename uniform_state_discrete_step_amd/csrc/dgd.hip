@@ -1263,6 +1263,42 @@ __device__ void sc_sort_desc(uint64_t* buf, int n) {
   }
 }
 
+// Descending bitonic sort of the 64 R keys one wave holds, key i = lane R + r
+// in v[r]: compare-exchanges inside a lane for distances below R, across
+// lanes (by shuffle) above.  No barriers.
+template <int R>
+__device__ __forceinline__ void wave_sort_desc(uint64_t (&v)[R]) {
+  const int lane = threadIdx.x & 63;
+  constexpr int N = 64 * R;
+#pragma unroll
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          if ((r ^ j) > r) {
+            const int i = lane * R + r;
+            const bool desc = (i & k) == 0;
+            const uint64_t x = v[r], y = v[r ^ j];
+            const bool swap = desc ? (x < y) : (x > y);
+            v[r] = swap ? y : x;
+            v[r ^ j] = swap ? x : y;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          const int i = lane * R + r;
+          const uint64_t o = __shfl_xor(v[r], j / R);
+          const bool keep_max = ((i & j) == 0) == ((i & k) == 0);
+          v[r] = keep_max ? max(v[r], o) : min(v[r], o);
+        }
+      }
+    }
+  }
+}
+
 // Tempered logit of vocabulary id v for one position, recomputed from the
 // packed table: an fp32 dot product in hidden order, then the same
 // temperature (or softcap) transform as the projection's epilogue.
@@ -1270,21 +1306,29 @@ __device__ float sc_logit(const ScArgs& a, const uint16_t* hrow, int v) {
   const int nk = packed_chunks(a.d);
   const int rg = v / kPackRows, f = (v % kPackRows) / 32, lv = v % 32;
   float acc = 0.f;
-  for (int c = 0; c < nk; ++c) {
+  // two chunks per round, their 16 table pieces and 16 hidden pieces loaded
+  // before any product (pieces past d are skipped; sums stay in hidden order)
+  for (int c0 = 0; c0 < nk; c0 += 2) {
+    u32x4_t w[16], x[16];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const int k0 = c * kKChunk + 32 * h + 8 * s;
-        if (k0 >= a.d) continue;
+    for (int q = 0; q < 16; ++q) {
+      const int c = c0 + q / 8, h = (q / 4) % 2, s = q % 4;
+      const int k0 = c * kKChunk + 32 * h + 8 * s;
+      if (c < nk && k0 < a.d) {
         const size_t u = ((((size_t)rg * nk + c) * 4 + s) * 2 + f) * 64 + lv + 32 * h;
-        const u32x4_t w = *(const u32x4_t*)(a.W + u * 8);
-        const u32x4_t x = *(const u32x4_t*)(hrow + k0);
+        w[q] = *(const u32x4_t*)(a.W + u * 8);
+        x[q] = *(const u32x4_t*)(hrow + k0);
+      } else {
+        w[q] = u32x4_t{0u, 0u, 0u, 0u};
+        x[q] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc = fmaf(__uint_as_float(x[j] << 16), __uint_as_float(w[j] << 16), acc);
-          acc = fmaf(__uint_as_float(x[j] & 0xffff0000u), __uint_as_float(w[j] & 0xffff0000u), acc);
-        }
+    for (int q = 0; q < 16; ++q)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = fmaf(__uint_as_float(x[q][j] << 16), __uint_as_float(w[q][j] << 16), acc);
+        acc = fmaf(__uint_as_float(x[q][j] & 0xffff0000u), __uint_as_float(w[q][j] & 0xffff0000u), acc);
       }
   }
   return a.cap ? softcap_bits(acc, a.cap_in, a.cap_out) : __fmul_rn(acc, a.c2);
@@ -1295,6 +1339,7 @@ __global__ void __launch_bounds__(kThreads) k_sc_topk(const ScArgs a) {
   __shared__ uint64_t sbuf[kScSortMax];
   __shared__ uint64_t tmax[kThreads];
   __shared__ int s_cnt;
+  __shared__ uint64_t s_bound;
   __shared__ uint64_t s_tagged;
   const int row = blockIdx.x;
   if (a.done[row / a.L]) return;
@@ -1320,25 +1365,44 @@ __global__ void __launch_bounds__(kThreads) k_sc_topk(const ScArgs a) {
   const uint16_t* hrow = a.H + (size_t)row * a.d;
   __syncthreads();
   for (;;) {
-    // ---- select: bound from the per-thread maxima, then sort what is above it
+    // ---- select: bound from the per-thread maxima (sorted by wave 0), then
+    // sort what is above it (one wave when it fits, else the whole block)
     uint64_t mx = 0;
     for (int i = tid; i < npool; i += kThreads) mx = max(mx, pool[i]);
     tmax[tid] = mx;
     if (tid == 0) s_cnt = 0;
     __syncthreads();
-    sc_sort_desc(tmax, kThreads);
-    const uint64_t bound = tmax[a.K - 1];
+    if (tid < 64) {
+      uint64_t v[kThreads / 64];
+#pragma unroll
+      for (int r = 0; r < kThreads / 64; ++r) v[r] = tmax[tid * (kThreads / 64) + r];
+      wave_sort_desc(v);
+#pragma unroll
+      for (int r = 0; r < kThreads / 64; ++r)
+        if (tid * (kThreads / 64) + r == a.K - 1) s_bound = v[r];
+    }
+    __syncthreads();
+    const uint64_t bound = s_bound;
     for (int i = tid; i < npool; i += kThreads) {
       const uint64_t k = pool[i];
       if (k != 0 && k >= bound) sbuf[atomicAdd(&s_cnt, 1)] = k;
     }
     __syncthreads();
     const int cnt = s_cnt;
-    int n = 64;
-    while (n < cnt) n <<= 1;
-    for (int i = cnt + tid; i < n; i += kThreads) sbuf[i] = 0;
-    __syncthreads();
-    sc_sort_desc(sbuf, n);
+    if (cnt <= 64) {
+      if (tid < 64) {
+        uint64_t v[1] = {tid < cnt ? sbuf[tid] : 0ull};
+        wave_sort_desc(v);
+        sbuf[tid] = v[0];
+      }
+      __syncthreads();
+    } else {
+      int n = 128;
+      while (n < cnt) n <<= 1;
+      for (int i = cnt + tid; i < n; i += kThreads) sbuf[i] = 0;
+      __syncthreads();
+      sc_sort_desc(sbuf, n);
+    }
     // ---- a tagged candidate whose value reaches the K-th selected value:
     // its list may have dropped values as large as its own (the largest such
     // key is taken; none, and the selection is exact)
