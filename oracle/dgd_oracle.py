@@ -53,6 +53,10 @@ pages this work follows; citations give page and section):
 8. A new block starts from uniform tokens (Philox word 0 of counter
    (0, p_abs, block, 2)); earlier blocks are never touched; the schedule
    restarts for each block (node page, gen_length row).
+10. Typed decisions (TensorSharp doc, "1. Origin and intent": label
+   probabilities read from a canvas in one denoising step through a sparse
+   output projection): logits of a given list of label ids only, and their
+   probabilities normalised over that list.
 9. Self-conditioning input for the next forward (walkthrough, "Complete
    DiffusionGemma model" and "Denoise, stage, commit, and generate": the
    decoder receives the previous step's tempered probabilities P and forms
@@ -326,6 +330,20 @@ def sc_embed(prob: np.ndarray, ids: np.ndarray, W_bits: np.ndarray, scale: float
     p16 = bf16_to_f64(round_bf16(np.asarray(prob, dtype=np.float64)))
     E = bf16_to_f64(W_bits[np.asarray(ids, dtype=np.int64)])     # [rows, K, d]
     return round_bf16(float(scale) * (p16[:, :, None] * E).sum(axis=1))
+
+
+# ----------------------------------------------------------------------------
+# 10. sparse label read
+# ----------------------------------------------------------------------------
+def label_probs(H_bits: np.ndarray, W_bits: np.ndarray, labels, T: float, softcap_c: float = 0.0):
+    """Logits of the label ids only, z[r, l] = H[r] . W[labels[l]] (then the
+    softcap c tanh(z / c) when c > 0), and p[r, l] = softmax over the labels
+    of z / T.  Returns (z float64 [rows, n], p float64 [rows, n])."""
+    labels = np.asarray(labels, dtype=np.int64)
+    z = softcap(projection(H_bits, W_bits[labels]), softcap_c)
+    x = z / float(T)
+    e = np.exp(x - x.max(axis=1, keepdims=True))
+    return z, e / e.sum(axis=1, keepdims=True)
 
 
 # ----------------------------------------------------------------------------

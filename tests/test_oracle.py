@@ -383,6 +383,52 @@ def test_sc_embed_is_exact_on_dyadic_inputs():
 
 
 # ----------------------------------------------------------------------------
+# sparse label read
+# ----------------------------------------------------------------------------
+def test_label_probs_closed_forms():
+    rng = np.random.default_rng(14)
+    d, V = 16, 40
+    W = bf16(rng.standard_normal((V, d)))
+    H = bf16(rng.standard_normal((3, d)))
+    # identical label rows: equal probabilities
+    Weq = W.copy()
+    Weq[[5, 9, 30]] = W[2]
+    _, p = O.label_probs(H, Weq, [2, 5, 9, 30], 0.7)
+    assert np.allclose(p, 0.25, rtol=1e-15)
+    # two labels: the logistic function of the tempered difference
+    z, p = O.label_probs(H, W, [3, 17], 0.5)
+    zz = O.projection(H, W)
+    assert np.array_equal(z, zz[:, [3, 17]])
+    assert np.allclose(p[:, 0], 1.0 / (1.0 + np.exp(-(zz[:, 3] - zz[:, 17]) / 0.5)), rtol=1e-14)
+    assert np.allclose(p.sum(axis=1), 1.0, rtol=1e-15)
+
+
+def test_label_probs_are_exact_integer_logits():
+    rng = np.random.default_rng(15)
+    Hi = rng.integers(-3, 4, size=(2, 40))
+    Wi = rng.integers(-3, 4, size=(30, 40))
+    labels = [29, 0, 7]
+    z, _ = O.label_probs(bf16(Hi), bf16(Wi), labels, 1.0)
+    assert np.array_equal(z, (Hi @ Wi[labels].T).astype(np.float64))
+
+
+def test_label_probs_on_the_top_k_agree_with_the_top_k_probabilities():
+    # labels = a position's top K: the label law is the top-K law renormalised
+    rng = np.random.default_rng(16)
+    V, d, T, K = 300, 24, 0.6, 12
+    W = bf16(rng.standard_normal((V, d)))
+    H = bf16(rng.standard_normal((1, d)) * 3)
+    z = O.projection(H, W)
+    prob, ids, _ = O.sc_topk(z, T, K)
+    zl, p = O.label_probs(H, W, ids[0], T)
+    assert np.allclose(p[0], prob[0] / prob[0].sum(), rtol=1e-12)
+    # and the softcap applies to the logits before the temperature
+    zc, pc = O.label_probs(H, W, ids[0], T, softcap_c=2.0)
+    assert np.allclose(zc, 2.0 * np.tanh(zl / 2.0), rtol=1e-15)
+    assert np.all(np.abs(zc) < 2.0)
+
+
+# ----------------------------------------------------------------------------
 # entropy and argmax
 # ----------------------------------------------------------------------------
 def test_entropy_of_uniform_row_is_log_v(golden_dir):
