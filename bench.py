@@ -111,6 +111,9 @@ def main():
                          "(c = 30) after it")
     ap.add_argument("--sc-topk", type=int, default=0,
                     help="self-conditioning top-K per position (0 = off), plus the embedding sum")
+    ap.add_argument("--label-read", type=int, default=0,
+                    help="also time the sparse label read (dgd_label_probs) of this many labels "
+                         "over the workload's positions")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed loop (for rocprofv3 runs)")
@@ -264,6 +267,24 @@ def main():
         "step_frac_of_hbm_floor": (steps_per_s * alg_bytes) / (HBM_PEAK_GBS * 1e9),
         "roofline": roof,
     }
+    if args.label_read:
+        n = args.label_read
+        labels = [int(v) for v in np.linspace(0, wl.V - 1, n).astype(np.int64)]
+        M = wl.B * wl.L
+        probs = torch.empty(M * n, dtype=torch.float32, device=dev)
+        H0 = Hd[0, 0].reshape(-1)
+        dgd.dgd_label_probs(H0, M, Wd, layout, wl.V, wl.d, labels, 1.0, 0.0, None, probs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 200
+        e0.record()
+        for _ in range(reps):
+            dgd.dgd_label_probs(H0, M, Wd, layout, wl.V, wl.d, labels, 1.0, 0.0, None, probs)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / reps * 1e3
+        out["label_read"] = {"n_labels": n, "positions": M, "us_per_call": us,
+                             "table_bytes_read": n * wl.d * 2, "vocab_layout": args.layout}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on one step")
         out["cpu_baseline"] = cpu_baseline(wl, W, Hs, tail, args.sc_topk)

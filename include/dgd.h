@@ -83,7 +83,10 @@ typedef uint16_t dgd_bf16;
 #define DGD_VOCAB_PACKED 1
 
 /* Largest self-conditioning top-K (dgd_ctx.sc_topk, dgd_sc_embed). */
-#define DGD_SC_MAX_TOPK 32  /* the output of dgd_pack_vocab() (MFMA fragment order)      */
+#define DGD_SC_MAX_TOPK 32
+
+/* Most labels one dgd_label_probs call reads. */
+#define DGD_MAX_LABELS 512  /* the output of dgd_pack_vocab() (MFMA fragment order)      */
 
 /* Sampler knobs (node page "Inputs"; TensorSharp doc "3. Sampler contract").
  * Ranges are checked on every call:
@@ -253,6 +256,26 @@ int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas,
 int dgd_sc_embed(const float* sc_prob, const int32_t* sc_id, int32_t rows, int32_t K,
                  const dgd_bf16* W_vocab, int32_t vocab_layout, int32_t V, int32_t d, float scale,
                  dgd_bf16* out, void* stream);
+
+/* Sparse label read for typed decisions (TensorSharp doc, "1. Origin and
+ * intent": label probabilities read from a canvas in one denoising step
+ * through a sparse output projection):
+ *   logits[r][l] = z = H[r] . E[labels[l]]  (fp32 sum), then c tanh(z / c)
+ *                  when softcap c > 0
+ *   probs[r][l]  = softmax over l of logits[r][l] / temperature
+ * Only the label rows of the table are read; the probabilities are
+ * normalised over the labels, not over the vocabulary.
+ *   H          device bf16[rows*d], 16-byte aligned (rows that already went
+ *              through the model's output norm, e.g. dgd_ctx.norm_h)
+ *   W_vocab    device, the table in vocab_layout (rows or packed), 16-B aligned
+ *   labels     HOST int32[n_labels], each in [0, V), 1 <= n_labels <= DGD_MAX_LABELS
+ *              (repeats allowed)
+ *   temperature  finite, >= 1e-4;  softcap  0 or in [0.01, 10000]
+ *   logits     device float[rows*n_labels] or NULL; probs device float[rows*n_labels]
+ * Enqueued on `stream`; 0 or a negative DGD_E* code. */
+int dgd_label_probs(const dgd_bf16* H, int32_t rows, const dgd_bf16* W_vocab, int32_t vocab_layout,
+                    int32_t V, int32_t d, const int32_t* labels, int32_t n_labels, float temperature,
+                    float softcap, float* logits, float* probs, void* stream);
 
 /* Size in bytes of the packed vocabulary table for (V, d):
  * ceil(V/64)*64 * ceil(d/64)*64 * 2; 0 if V or d is outside the limits. */

@@ -195,6 +195,35 @@ def test_sc_embed_refusals(lib):
         assert dgd.dgd_last_error()
 
 
+def test_label_probs_refusals(lib):
+    f = lib.dgd_label_probs
+
+    def call(labels=(1, 2), **kw):
+        arr = (ctypes.c_int32 * max(len(labels), 1))(*labels)
+        args = dict(H=FAKE, rows=4, W=FAKE, layout=0, V=1024, d=64, n=len(labels), T=1.0, cap=0.0,
+                    logits=None, probs=FAKE, stream=None)
+        args.update(kw)
+        return f(args["H"], args["rows"], args["W"], args["layout"], args["V"], args["d"],
+                 kw.get("labels_ptr", arr), args["n"], args["T"], args["cap"], args["logits"],
+                 args["probs"], args["stream"])
+
+    assert call(rows=0) == dgd.DGD_OK                      # nothing to do, nothing read
+    cases = [(dict(H=None), dgd.DGD_EINVAL), (dict(W=None), dgd.DGD_EINVAL),
+             (dict(probs=None), dgd.DGD_EINVAL), (dict(labels_ptr=None), dgd.DGD_EINVAL),
+             (dict(rows=-1), dgd.DGD_EINVAL), (dict(V=0), dgd.DGD_EUNSUPPORTED),
+             (dict(d=12), dgd.DGD_EUNSUPPORTED), (dict(layout=3), dgd.DGD_EINVAL),
+             (dict(n=0), dgd.DGD_EINVAL), (dict(T=0.0), dgd.DGD_EINVAL),
+             (dict(T=float("inf")), dgd.DGD_EINVAL), (dict(cap=-2.0), dgd.DGD_EINVAL),
+             (dict(cap=1e5), dgd.DGD_EINVAL), (dict(H=FAKE + 2), dgd.DGD_EINVAL),
+             (dict(W=FAKE + 8), dgd.DGD_EINVAL)]
+    for kw, code in cases:
+        assert call(**kw) == code, kw
+        assert dgd.dgd_last_error()
+    assert call(labels=(1, 1024)) == dgd.DGD_EINVAL       # id past V
+    assert call(labels=(-1,)) == dgd.DGD_EINVAL
+    assert call(labels=tuple(range(513))) == dgd.DGD_EINVAL
+
+
 def test_tail_overlap_is_checked_over_every_step_of_a_run(lib):
     # H_steps spans N steps of B*L*d bf16 values; norm_h just past step 0 still overlaps
     p = dgd.make_params(N=8)

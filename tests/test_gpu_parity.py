@@ -276,6 +276,50 @@ def test_sc_embed_matches_the_oracle(dev, layout):
 
 
 # ----------------------------------------------------------------------------
+# sparse label read
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("case", [
+    dict(V=1024, d=64, rows=16, labels=[3, 17], T=1.0, cap=0.0),
+    dict(V=1001, d=72, rows=37, labels=[1000, 0, 500, 500, 7], T=0.45, cap=0.0),
+    dict(V=32768, d=1024, rows=256, labels=list(range(0, 32768, 64)), T=0.8, cap=30.0),
+    dict(V=4096, d=4104, rows=3, labels=[4095, 1, 2, 3], T=0.6, cap=5.0),
+    dict(V=262144, d=2816, rows=64, labels=[11, 262143, 130000, 5, 77777, 250000], T=1.0, cap=0.0),
+], ids=["two", "ragged_repeats", "512_labels_capped", "wide_hidden", "gemma_vocab"])
+@pytest.mark.parametrize("layout", [0, 1], ids=["rows", "packed"])
+def test_label_probs_match_the_oracle(dev, case, layout):
+    import torch
+    from uniform_state_discrete_step_amd import dgd
+    from uniform_state_discrete_step_amd.inputs import make_h, make_w
+    V, d, rows, labels = case["V"], case["d"], case["rows"], case["labels"]
+    if V > 65536:                      # only the label rows matter: zero the rest
+        W = np.zeros((V, d), dtype=np.uint16)
+        W[labels] = make_w(len(labels), d, 31)
+    else:
+        W = make_w(V, d, 31)
+    H = make_h(rows, d, 31, 0, 0)
+    Wt = torch.from_numpy(W.view(np.int16)).to(dev)
+    if layout == 1:
+        Wt = dgd.pack_vocab(Wt, V, d)
+    Hd = torch.from_numpy(H.view(np.int16)).to(dev)
+    n = len(labels)
+    logits = torch.empty(rows * n, dtype=torch.float32, device=dev)
+    probs = torch.empty(rows * n, dtype=torch.float32, device=dev)
+    dgd.dgd_label_probs(Hd, rows, Wt, layout, V, d, labels, case["T"], case["cap"], logits, probs)
+    torch.cuda.synchronize()
+    zg = logits.cpu().numpy().reshape(rows, n).astype(np.float64)
+    pg = probs.cpu().numpy().reshape(rows, n).astype(np.float64)
+    zo, po = O.label_probs(H, W, labels, case["T"], case["cap"])
+    scale = np.maximum(np.abs(zo), np.sqrt(np.mean(zo * zo, axis=1, keepdims=True)))
+    zerr = (np.abs(zg - zo) / np.maximum(scale, 1e-30)).max()
+    perr = (np.abs(pg - po) / np.maximum(po, 1e-30)).max()
+    print(f"\n[labels n={n} V={V} d={d} layout={layout}] logit rel err {zerr:.2e}, "
+          f"prob rel err {perr:.2e}", flush=True)
+    assert zerr <= TOL_LOGIT_REL
+    assert np.all(np.abs(pg - po) <= 1e-3 * po + 1e-30)
+    assert np.allclose(pg.sum(axis=1), 1.0, atol=1e-5)
+
+
+# ----------------------------------------------------------------------------
 def _logit_check(wl, dev, W, Hs, steps, layout, tail=None):
     import torch
     ls = Lockstep(wl, W, Hs, dev, logits=True, layout=layout, tail=tail)

@@ -1532,6 +1532,95 @@ __global__ void __launch_bounds__(kThreads) k_sc_embed(const float* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_label: the sparse label read
+// ---------------------------------------------------------------------------
+// One workgroup per row.  Wave w takes labels w, w + 4, ...: its lanes take
+// 16-byte pieces of the hidden dimension (consecutive pieces on consecutive
+// lanes), add 8 fp32 products each, and a butterfly sums the lanes.  The
+// logits (capped when asked) go to LDS; the block then forms the tempered
+// softmax over the labels in bits: p = 2^(x2 - m) / S with x2 = z * log2(e) / T.
+struct LabelArgs {
+  const uint16_t* H;      // [rows][d]
+  const uint16_t* W;      // table, row-major or packed
+  float* logits;          // [rows][n] or null
+  float* probs;           // [rows][n]
+  int32_t rows, V, d, n, packed;
+  float c2, cap_in, cap;  // cap: c (0 = off)
+  int32_t labels[DGD_MAX_LABELS];
+};
+
+__device__ __forceinline__ float block_max_f32(float v, float* red) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float out = red[0];
+#pragma unroll
+  for (int w = 1; w < kWaves; ++w) out = fmaxf(out, red[w]);
+  __syncthreads();
+  return out;
+}
+
+__device__ __forceinline__ float block_sum_f32(float v, float* red) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float out = 0.f;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) out += red[w];
+  __syncthreads();
+  return out;
+}
+
+__global__ void __launch_bounds__(kThreads) k_label(const LabelArgs a) {
+  __shared__ float zs[DGD_MAX_LABELS];
+  __shared__ float red[kWaves];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint16_t* hrow = a.H + (size_t)row * a.d;
+  const int nk = packed_chunks(a.d), n8 = a.d / 8;
+  for (int l = wave; l < a.n; l += kWaves) {
+    const int v = a.labels[l];
+    const int rg = v / kPackRows, f = (v % kPackRows) / 32, lv = v % 32;
+    float acc = 0.f;
+    for (int q = lane; q < n8; q += 64) {
+      const int k0 = q * 8;
+      size_t off;
+      if (a.packed) {
+        const int c = k0 / kKChunk, h = (k0 % kKChunk) / 32, sidx = (k0 % 32) / 8;
+        off = (((((size_t)rg * nk + c) * 4 + sidx) * 2 + f) * 64 + lv + 32 * h) * 8;
+      } else {
+        off = (size_t)v * a.d + k0;
+      }
+      const u32x4_t w = *(const u32x4_t*)(a.W + off);
+      const u32x4_t x = *(const u32x4_t*)(hrow + k0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = fmaf(__uint_as_float(x[j] << 16), __uint_as_float(w[j] << 16), acc);
+        acc = fmaf(__uint_as_float(x[j] & 0xffff0000u), __uint_as_float(w[j] & 0xffff0000u), acc);
+      }
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (lane == 0) zs[l] = a.cap != 0.f ? softcap_bits(acc, a.cap_in, a.cap) : acc;
+  }
+  __syncthreads();
+  float m = -INFINITY;
+  for (int l = tid; l < a.n; l += kThreads) m = fmaxf(m, zs[l] * a.c2);
+  m = block_max_f32(m, red);
+  float sum = 0.f;
+  for (int l = tid; l < a.n; l += kThreads) sum += fexp2(zs[l] * a.c2 - m);
+  sum = block_sum_f32(sum, red);
+  for (int l = tid; l < a.n; l += kThreads) {
+    a.probs[(size_t)row * a.n + l] = fexp2(zs[l] * a.c2 - m) / sum;
+    if (a.logits) a.logits[(size_t)row * a.n + l] = zs[l];
+  }
+}
+
 // Grid (B): the commit of every canvas that is not done, one workgroup each
 // (the kernel boundary after k_merge publishes the per-position results).
 __global__ void __launch_bounds__(kThreads) k_commit(const CommitArgs a) {
@@ -2061,6 +2150,40 @@ int dgd_sc_embed(const float* sc_prob, const int32_t* sc_id, int32_t rows, int32
                      W_vocab, vocab_layout == DGD_VOCAB_PACKED ? 1 : 0, V, d, scale, out);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? DGD_OK : hip_fail(e, "k_sc_embed launch");
+}
+
+int dgd_label_probs(const dgd_bf16* H, int32_t rows, const dgd_bf16* W_vocab, int32_t vocab_layout,
+                    int32_t V, int32_t d, const int32_t* labels, int32_t n_labels, float temperature,
+                    float softcap, float* logits, float* probs, void* stream) {
+  g_err.clear();
+  if (!H || !W_vocab || !labels || !probs) return fail(DGD_EINVAL, "H/W_vocab/labels/probs is NULL");
+  if (rows < 0) return fail(DGD_EINVAL, "rows=%d < 0", rows);
+  if (V < 1 || V > DGD_MAX_VOCAB) return fail(DGD_EUNSUPPORTED, "V=%d outside [1, 2^24]", V);
+  if (d < 8 || d > DGD_MAX_HIDDEN || d % 8 != 0)
+    return fail(DGD_EUNSUPPORTED, "d=%d must be a multiple of 8 in [8, %d]", d, DGD_MAX_HIDDEN);
+  if (vocab_layout != DGD_VOCAB_ROWS && vocab_layout != DGD_VOCAB_PACKED)
+    return fail(DGD_EINVAL, "vocab_layout=%d is neither DGD_VOCAB_ROWS nor DGD_VOCAB_PACKED", vocab_layout);
+  if (n_labels < 1 || n_labels > DGD_MAX_LABELS)
+    return fail(DGD_EINVAL, "n_labels=%d outside [1, %d]", n_labels, DGD_MAX_LABELS);
+  for (int i = 0; i < n_labels; ++i)
+    if (labels[i] < 0 || labels[i] >= V) return fail(DGD_EINVAL, "labels[%d]=%d outside [0, V)", i, labels[i]);
+  if (!std::isfinite(temperature) || temperature < kMinTemperature)
+    return fail(DGD_EINVAL, "temperature=%g must be finite and >= %g", temperature, kMinTemperature);
+  if (!std::isfinite(softcap) || (softcap != 0.f && (softcap < 0.01f || softcap > 10000.f)))
+    return fail(DGD_EINVAL, "softcap=%g must be 0 or in [0.01, 10000]", softcap);
+  if (!aligned16(H) || !aligned16(W_vocab)) return fail(DGD_EINVAL, "H/W_vocab is not 16-byte aligned");
+  if (rows == 0) return DGD_OK;
+  LabelArgs la{};
+  la.H = H; la.W = W_vocab; la.logits = logits; la.probs = probs;
+  la.rows = rows; la.V = V; la.d = d; la.n = n_labels;
+  la.packed = vocab_layout == DGD_VOCAB_PACKED ? 1 : 0;
+  la.c2 = (float)(kLog2e / (double)temperature);
+  la.cap = softcap;
+  la.cap_in = softcap != 0.f ? (float)(1.0 / softcap) : 0.f;
+  for (int i = 0; i < n_labels; ++i) la.labels[i] = labels[i];
+  hipLaunchKernelGGL(k_label, dim3((unsigned)rows), dim3(kThreads), 0, (hipStream_t)stream, la);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_label launch");
 }
 
 int dgd_debug_gumbel(const uint32_t* words, float* out, int64_t n, void* stream) {

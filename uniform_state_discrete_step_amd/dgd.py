@@ -27,7 +27,8 @@ DGD_VOCAB_ROWS = 0
 DGD_VOCAB_PACKED = 1
 
 EXPORTED = ("dgd_state_bytes", "dgd_workspace_bytes", "dgd_init_block", "dgd_step", "dgd_run",
-            "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_sc_embed", "dgd_debug_gumbel",
+            "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_sc_embed", "dgd_label_probs",
+            "dgd_debug_gumbel",
             "dgd_last_error")
 
 
@@ -115,6 +116,12 @@ def load_library(path: str = LIB_PATH):
     lib.dgd_sc_embed.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]
+    lib.dgd_label_probs.restype = ctypes.c_int
+    lib.dgd_label_probs.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p,
+                                    ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
+                                    ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p]
     lib.dgd_debug_gumbel.restype = ctypes.c_int
     lib.dgd_debug_gumbel.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                      ctypes.c_void_p]
@@ -315,6 +322,17 @@ def dgd_sc_embed(sc_prob, sc_id, rows: int, K: int, W_vocab, vocab_layout: int, 
     _check(load_library().dgd_sc_embed(_ptr(sc_prob, 4), _ptr(sc_id, 4), int(rows), int(K),
                                        _ptr(W_vocab, 2), int(vocab_layout), int(V), int(d),
                                        float(scale), _ptr(out, 2), _stream_handle(stream)))
+
+
+def dgd_label_probs(H, rows: int, W_vocab, vocab_layout: int, V: int, d: int, labels,
+                    temperature: float, softcap: float, logits, probs, stream=None):
+    """labels: host sequence of ints; logits may be None."""
+    lab = np.asarray(labels, dtype=np.int32).reshape(-1)
+    arr = (ctypes.c_int32 * len(lab))(*[int(x) for x in lab])
+    _check(load_library().dgd_label_probs(_ptr(H, 2), int(rows), _ptr(W_vocab, 2),
+                                          int(vocab_layout), int(V), int(d), arr, len(lab),
+                                          float(temperature), float(softcap), _ptr(logits, 4),
+                                          _ptr(probs, 4), _stream_handle(stream)))
 
 
 def dgd_debug_gumbel(words, out, stream=None):
