@@ -53,6 +53,12 @@ pages this work follows; citations give page and section):
 8. A new block starts from uniform tokens (Philox word 0 of counter
    (0, p_abs, block, 2)); earlier blocks are never touched; the schedule
    restarts for each block (node page, gen_length row).
+11. A 4-bit table (the pages run quantized checkpoints: INT4 W4A16 and
+   GGUF K-quant files, ComfyUI pack "What works today" and "Downloads"):
+   groups of 32 hidden elements of a row share a bf16 scale s and minimum m,
+   each element keeps a 4-bit code q, and the step uses the table
+   w = bf16(fp32(s) * q + fp32(m)) (one float32 rounding, then nearest-even
+   to bf16).  Everything after the table is unchanged.
 10. Typed decisions (TensorSharp doc, "1. Origin and intent": label
    probabilities read from a canvas in one denoising step through a sparse
    output projection): logits of a given list of label ids only, and their
@@ -330,6 +336,32 @@ def sc_embed(prob: np.ndarray, ids: np.ndarray, W_bits: np.ndarray, scale: float
     p16 = bf16_to_f64(round_bf16(np.asarray(prob, dtype=np.float64)))
     E = bf16_to_f64(W_bits[np.asarray(ids, dtype=np.int64)])     # [rows, K, d]
     return round_bf16(float(scale) * (p16[:, :, None] * E).sum(axis=1))
+
+
+# ----------------------------------------------------------------------------
+# 11. 4-bit table: dequantization
+# ----------------------------------------------------------------------------
+Q4_GROUP = 32
+
+
+def dequant_q4(codes: np.ndarray, scales: np.ndarray, mins: np.ndarray) -> np.ndarray:
+    """The bf16 table a 4-bit table stands for.
+
+    codes uint8 [V, d/2]: element 2i in the low nibble of byte i, element
+    2i + 1 in the high nibble; scales, mins bf16 bits [V, d/32].  Each value
+    is s * q + m in float32 (the product of a bf16 and a 4-bit integer is
+    exact in float32, so one rounding), then rounded to bf16.
+    """
+    codes = np.asarray(codes, dtype=np.uint8)
+    V, half = codes.shape
+    d = 2 * half
+    q = np.empty((V, d), dtype=np.float32)
+    q[:, 0::2] = codes & 0x0F
+    q[:, 1::2] = codes >> 4
+    s = np.repeat(bf16_to_f64(scales).astype(np.float32), Q4_GROUP, axis=1)
+    m = np.repeat(bf16_to_f64(mins).astype(np.float32), Q4_GROUP, axis=1)
+    w32 = s * q + m                               # float32: exact product, one rounding
+    return round_bf16(w32.astype(np.float64))
 
 
 # ----------------------------------------------------------------------------

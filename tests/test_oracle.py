@@ -429,6 +429,43 @@ def test_label_probs_on_the_top_k_agree_with_the_top_k_probabilities():
 
 
 # ----------------------------------------------------------------------------
+# 4-bit table
+# ----------------------------------------------------------------------------
+def test_dequant_q4_by_hand():
+    # one row of 32 elements: codes 0..15 then 15..0; scale 0.5, min -2
+    q = np.array(list(range(16)) + list(range(15, -1, -1)), dtype=np.uint8)
+    codes = (q[0::2] | (q[1::2] << 4))[None, :]
+    w = O.bf16_to_f64(O.dequant_q4(codes, bf16([[0.5]]), bf16([[-2.0]])))[0]
+    assert np.array_equal(w, 0.5 * q - 2.0)           # every value exact in bf16
+    # element order: low nibble first
+    c = np.zeros((1, 16), dtype=np.uint8)
+    c[0, 0] = 0x31                                     # element 0 -> 1, element 1 -> 3
+    w = O.bf16_to_f64(O.dequant_q4(c, bf16([[1.0]]), bf16([[0.0]])))[0]
+    assert w[0] == 1.0 and w[1] == 3.0 and not w[2:].any()
+
+
+def test_dequant_q4_rounds_once_to_nearest_even():
+    # s q + m = 1 + k 2^-8 lands halfway between bf16 neighbours for odd k
+    c = np.zeros((1, 16), dtype=np.uint8)
+    c[0, 0] = 0x31                                     # q = 1, 3
+    w = O.dequant_q4(c, bf16([[2.0 ** -8]]), bf16([[1.0]]))[0]
+    assert w[0] == 0x3F80                              # 1 + 2^-8 -> 1 (even)
+    assert w[1] == 0x3F82                              # 1 + 3 2^-8 -> 1 + 2^-6 (even)
+    assert np.all(w[2:] == 0x3F80)                     # q = 0: the minimum itself
+
+
+def test_quantized_table_is_close_to_the_original():
+    from uniform_state_discrete_step_amd.inputs import make_w, quantize_q4
+    W = make_w(64, 96, 3)
+    codes, sc, mn = quantize_q4(W)
+    Wq = O.bf16_to_f64(O.dequant_q4(codes, sc, mn))
+    W0 = O.bf16_to_f64(W)
+    step = np.repeat(O.bf16_to_f64(sc), 32, axis=1)
+    # within half a step (plus the bf16 roundings of scale, minimum and value)
+    assert np.all(np.abs(Wq - W0) <= 0.5 * step + 0.02 * np.abs(W0) + 1e-3)
+
+
+# ----------------------------------------------------------------------------
 # entropy and argmax
 # ----------------------------------------------------------------------------
 def test_entropy_of_uniform_row_is_log_v(golden_dir):

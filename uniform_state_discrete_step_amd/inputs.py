@@ -18,6 +18,10 @@ tied [V x d] embedding table):
   ``default_rng([cfg_seed, 1, c, b*N + s])``; first L log-uniform row scales
   ``r = exp(U(ln lo, ln hi))``, then an [L, d] float32 standard normal; the row
   is ``r * z`` rounded to bfloat16.
+* A 4-bit table (for runs of the quantized stream): the bf16 table above,
+  quantized group by group (32 hidden elements): scale = bf16((max - min)/15)
+  (1 if the group is constant), min = bf16(min), codes = the nearest of
+  0..15 to (w - min) / scale.  Only a way to obtain realistic codes.
 * Output-norm weights [d] (only for runs with the lm-head tail): generator
   ``default_rng([cfg_seed, 2])``, log-uniform per channel in [lo, hi] (default
   [0.5, 8]), rounded to bfloat16.  The walkthrough prints no trained values.
@@ -168,3 +172,19 @@ def make_norm_weight(d: int, cfg_seed: int, scale=(0.5, 8.0)) -> np.ndarray:
     lo, hi = scale
     w = np.exp(rng.uniform(math.log(lo), math.log(hi), size=d)).astype(np.float32)
     return f32_to_bf16_bits(w)
+
+
+def quantize_q4(W_bits: np.ndarray):
+    """(codes uint8 [V, d/2], scales bf16 bits [V, d/32], mins bf16 bits [V, d/32])
+    of a bf16 table (see module docstring); d must be a multiple of 32."""
+    V, d = W_bits.shape
+    w = bf16_bits_to_f32(W_bits).reshape(V, d // 32, 32)
+    lo, hi = w.min(axis=2), w.max(axis=2)
+    scale = np.where(hi > lo, (hi - lo) / np.float32(15.0), np.float32(1.0)).astype(np.float32)
+    s_bits = f32_to_bf16_bits(scale)
+    m_bits = f32_to_bf16_bits(lo)
+    s = bf16_bits_to_f32(s_bits)[:, :, None]
+    m = bf16_bits_to_f32(m_bits)[:, :, None]
+    q = np.clip(np.rint((w - m) / s), 0, 15).astype(np.uint8).reshape(V, d)
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    return codes, s_bits, m_bits
