@@ -104,8 +104,9 @@ def main():
     ap.add_argument("--steps", type=int, default=480)
     ap.add_argument("--warmup", type=int, default=48)
     ap.add_argument("--workload", default="gemma_vocab")
-    ap.add_argument("--layout", choices=["packed", "rows"], default="packed",
-                    help="vocabulary table layout: packed once before timing (default) or row-major")
+    ap.add_argument("--layout", choices=["packed", "rows", "q4"], default="packed",
+                    help="vocabulary table layout: packed once before timing (default), row-major, "
+                         "or a 4-bit table (the synthetic table quantized in groups of 32)")
     ap.add_argument("--lm-head-tail", action="store_true",
                     help="output RMSNorm (eps 1e-6) before the projection and a logit softcap "
                          "(c = 30) after it")
@@ -130,7 +131,7 @@ def main():
 
     from uniform_state_discrete_step_amd import dgd
     from uniform_state_discrete_step_amd.inputs import (WORKLOADS, make_norm_weight,
-                                                        make_workload_arrays)
+                                                        make_workload_arrays, quantize_q4)
 
     wl = WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
@@ -139,11 +140,19 @@ def main():
     log(f"[bench] generated {wl.name} inputs in {time.perf_counter() - t0:.1f}s")
     Wd = torch.from_numpy(W.view(np.int16)).to(dev)
     W_rows = Wd
-    layout = dgd.DGD_VOCAB_PACKED if args.layout == "packed" else dgd.DGD_VOCAB_ROWS
+    layout = {"packed": dgd.DGD_VOCAB_PACKED, "rows": dgd.DGD_VOCAB_ROWS,
+              "q4": dgd.DGD_VOCAB_Q4}[args.layout]
     if layout == dgd.DGD_VOCAB_PACKED:
         # one-time rewrite of the table into the projection's streaming order
         Wd = dgd.pack_vocab(Wd, wl.V, wl.d)
         torch.cuda.synchronize()
+    elif layout == dgd.DGD_VOCAB_Q4:
+        codes, sc, mn = quantize_q4(W)
+        Wd = dgd.pack_vocab_q4(torch.from_numpy(codes.reshape(-1)).to(dev),
+                               torch.from_numpy(sc.reshape(-1).view(np.int16)).to(dev),
+                               torch.from_numpy(mn.reshape(-1).view(np.int16)).to(dev), wl.V, wl.d)
+        torch.cuda.synchronize()
+        log(f"[bench] quantized the table to 4 bits: {Wd.numel() / 1e9:.3f} GB")
     if not args.sc_topk:
         W_rows = None    # the row-major copy only serves the self-conditioning gather
     Hd = torch.from_numpy(Hs.view(np.int16)).to(dev)
@@ -220,7 +229,9 @@ def main():
     ctx.time_k1 = False
     k1_avg_s = k1_ms / max(k1_n, 1) * 1e-3
     M = wl.B * wl.L
-    alg_bytes = wl.V * wl.d * 2 + M * wl.d * 2
+    table_bytes = (dgd.dgd_q4_vocab_bytes(wl.V, wl.d) if layout == dgd.DGD_VOCAB_Q4
+                   else wl.V * wl.d * 2)
+    alg_bytes = table_bytes + M * wl.d * 2
     flops = 2.0 * M * wl.V * wl.d
     gbs = alg_bytes / k1_avg_s / 1e9
     tflops = flops / k1_avg_s / 1e12
@@ -231,9 +242,10 @@ def main():
              "frac": hbm_frac} if bound == "hbm" else
             {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": mfma_frac})
-    kname = "k_project_packed" if layout == dgd.DGD_VOCAB_PACKED else "k_project"
+    kname = "k_project" if layout == dgd.DGD_VOCAB_ROWS else "k_project_packed"
     traffic = (measured_traffic(kname)
-               if wl.name == "gemma_vocab" and not args.lm_head_tail and not args.sc_topk else None)
+               if wl.name == "gemma_vocab" and not args.lm_head_tail and not args.sc_topk
+               and layout == dgd.DGD_VOCAB_PACKED else None)
     roof.update({"traffic": traffic,
                  "kernel": kname, "kernel_avg_us": k1_avg_s * 1e6,
                  "kernel_launches": k1_n, "algorithmic_bytes_per_launch": alg_bytes,
@@ -287,7 +299,13 @@ def main():
                              "table_bytes_read": n * wl.d * 2, "vocab_layout": args.layout}
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on one step")
-        out["cpu_baseline"] = cpu_baseline(wl, W, Hs, tail, args.sc_topk)
+        W_cpu = W
+        if layout == dgd.DGD_VOCAB_Q4:
+            # the oracle steps on the bf16 table the 4-bit one stands for
+            # (dequantized once, outside the timing, as the GPU packs once)
+            from oracle import dgd_oracle as O
+            W_cpu = O.dequant_q4(codes, sc, mn)
+        out["cpu_baseline"] = cpu_baseline(wl, W_cpu, Hs, tail, args.sc_topk)
     print(json.dumps(out), flush=True)
 
 

@@ -81,6 +81,7 @@ typedef uint16_t dgd_bf16;
 /* Layouts of the vocabulary table W_vocab accepted by dgd_step / dgd_run. */
 #define DGD_VOCAB_ROWS   0  /* [V][d] row-major: the tied embedding table as is          */
 #define DGD_VOCAB_PACKED 1
+#define DGD_VOCAB_Q4     2
 
 /* Largest self-conditioning top-K (dgd_ctx.sc_topk, dgd_sc_embed). */
 #define DGD_SC_MAX_TOPK 32
@@ -133,7 +134,10 @@ typedef struct dgd_params {
  *   vocab_layout   DGD_VOCAB_ROWS (0) when W_vocab is the [V][d] table itself,
  *                  DGD_VOCAB_PACKED (1) when it is the output of dgd_pack_vocab()
  *                  for the same V and d (the faster path: every load of the
- *                  projection is a contiguous 1 KB MFMA fragment)
+ *                  projection is a contiguous 1 KB MFMA fragment),
+ *                  DGD_VOCAB_Q4 (2) when it is the output of dgd_pack_vocab_q4():
+ *                  a 4-bit table the projection dequantizes as it streams it
+ *                  (d a multiple of 32; no self-conditioning top-K)
  * Optional lm-head tail (walkthrough, "RMSNorm" and "Logit Softcapping";
  * TensorSharp doc, "2. Forward graph": output norm -> tied lm-head -> final
  * logit softcap).  Zero-initialised fields leave both off, and H is then
@@ -276,6 +280,26 @@ int dgd_sc_embed(const float* sc_prob, const int32_t* sc_id, int32_t rows, int32
 int dgd_label_probs(const dgd_bf16* H, int32_t rows, const dgd_bf16* W_vocab, int32_t vocab_layout,
                     int32_t V, int32_t d, const int32_t* labels, int32_t n_labels, float temperature,
                     float softcap, float* logits, float* probs, void* stream);
+
+/* A 4-bit table (the pages' quantized checkpoints: INT4 W4A16 and GGUF
+ * 4-bit files, ComfyUI pack "What works today" and "Downloads"): each row is
+ * cut into groups of 32 hidden elements sharing a bf16 scale s and minimum m;
+ * element k keeps a 4-bit code q and stands for
+ *   w = bf16( fp32(s) * q + fp32(m) )   (one fp32 rounding, then nearest-even)
+ * The step with ctx->vocab_layout = DGD_VOCAB_Q4 is the step on that table.
+ * dgd_q4_vocab_bytes: size of the streaming form, ceil(V/64)*64 rows x
+ * ceil(d/64) chunks x 40 bytes per 64 elements; 0 if V or d is outside the
+ * limits or d is not a multiple of 32.
+ * dgd_pack_vocab_q4 rewrites the natural form into it, once per table:
+ *   codes   device uint8[V*d/2]: element 2i of a row in the low nibble of byte
+ *           i, element 2i+1 in the high nibble; 16-byte aligned
+ *   scales, mins  device bf16[V*(d/32)], group g of row v at v*(d/32) + g
+ *   W_q4    device, dgd_q4_vocab_bytes(V, d) bytes, 16-byte aligned, written;
+ *           must not overlap the inputs
+ * Enqueued on `stream`; 0 or a negative DGD_E* code. */
+size_t dgd_q4_vocab_bytes(int32_t V, int32_t d);
+int dgd_pack_vocab_q4(const uint8_t* codes, const dgd_bf16* scales, const dgd_bf16* mins, void* W_q4,
+                      int32_t V, int32_t d, void* stream);
 
 /* Size in bytes of the packed vocabulary table for (V, d):
  * ceil(V/64)*64 * ceil(d/64)*64 * 2; 0 if V or d is outside the limits. */

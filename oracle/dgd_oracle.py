@@ -361,7 +361,16 @@ def dequant_q4(codes: np.ndarray, scales: np.ndarray, mins: np.ndarray) -> np.nd
     s = np.repeat(bf16_to_f64(scales).astype(np.float32), Q4_GROUP, axis=1)
     m = np.repeat(bf16_to_f64(mins).astype(np.float32), Q4_GROUP, axis=1)
     w32 = s * q + m                               # float32: exact product, one rounding
-    return round_bf16(w32.astype(np.float64))
+    return round_bf16_f32(w32)
+
+
+def round_bf16_f32(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bits, nearest with ties to even, on the bit
+    pattern: add 0x7FFF plus the lowest kept bit, drop the low 16 bits (finite
+    inputs).  The same rounding as round_bf16 for values float32 holds."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)       # finite: the sum stays below 2^32
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
 
 
 # ----------------------------------------------------------------------------

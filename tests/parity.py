@@ -32,6 +32,7 @@ import dataclasses
 import numpy as np
 
 from oracle import dgd_oracle as O
+from uniform_state_discrete_step_amd.inputs import quantize_q4
 
 TOL_ENTROPY = 1e-3
 BAND_ARGMAX = 1e-5
@@ -75,6 +76,16 @@ class Report:
                    if self.norm_rows else "")
                 + (f" sc rows={self.sc_rows} band={self.sc_band} recomputed parts="
                    f"{self.sc_recomputed}" if self.sc_rows else ""))
+
+
+def q4_device_table(W, V, d, device):
+    """The packed 4-bit form of a bf16 table (quantized on the host)."""
+    import torch
+    from uniform_state_discrete_step_amd import dgd
+    codes, sc, mn = quantize_q4(W)
+    return dgd.pack_vocab_q4(torch.from_numpy(codes.reshape(-1)).to(device),
+                             torch.from_numpy(sc.reshape(-1).view(np.int16)).to(device),
+                             torch.from_numpy(mn.reshape(-1).view(np.int16)).to(device), V, d)
 
 
 def ordered_bf16(bits) -> np.ndarray:
@@ -246,9 +257,15 @@ class Lockstep:
         self.dgd, self.torch = dgd, torch
         self.wl, self.W, self.Hs, self.dev = wl, W, Hs, device
         self.tail = tail
-        self.Wd = torch.from_numpy(W.view(np.int16)).to(device)
-        if layout == dgd.DGD_VOCAB_PACKED:
-            self.Wd = dgd.pack_vocab(self.Wd, wl.V, wl.d)
+        if layout == dgd.DGD_VOCAB_Q4:
+            # a 4-bit table: the GPU streams its packed form, the oracle
+            # steps on the bf16 table it stands for
+            self.Wd = q4_device_table(W, wl.V, wl.d, device)
+            self.W = W = O.dequant_q4(*quantize_q4(W))
+        else:
+            self.Wd = torch.from_numpy(W.view(np.int16)).to(device)
+            if layout == dgd.DGD_VOCAB_PACKED:
+                self.Wd = dgd.pack_vocab(self.Wd, wl.V, wl.d)
         self.Hd = torch.from_numpy(Hs.view(np.int16)).to(device)
         tkw = {}
         if tail is not None:

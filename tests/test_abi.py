@@ -113,8 +113,10 @@ def test_invalid_knobs_are_refused(lib, kw, code):
     (dict(workspace=None), dgd.DGD_EINVAL),
     (dict(workspace=FAKE * 16 + 8), dgd.DGD_EINVAL),
     (dict(workspace_bytes=100), dgd.DGD_EWORKSPACE),
-    (dict(vocab_layout=2), dgd.DGD_EINVAL),
+    (dict(vocab_layout=3), dgd.DGD_EINVAL),
     (dict(vocab_layout=-1), dgd.DGD_EINVAL),
+    (dict(vocab_layout=2, d=72), dgd.DGD_EUNSUPPORTED),        # 4-bit table: d % 32 != 0
+    (dict(vocab_layout=2, sc_topk=8, sc_prob=FAKE, sc_id=FAKE), dgd.DGD_EUNSUPPORTED),
 ])
 def test_invalid_shapes_and_buffers_are_refused(lib, kw, code):
     assert _step(lib, _ctx(**kw)) == code
@@ -170,6 +172,23 @@ def test_invalid_tail_is_refused(lib, kw):
 ])
 def test_invalid_self_conditioning_is_refused(lib, kw, code):
     assert _step(lib, _ctx(**kw)) == code
+    assert dgd.dgd_last_error()
+
+
+def test_q4_table_size_and_refusals(lib):
+    # 40 bytes per 64 elements: 32 of codes, 8 of scales and minima
+    assert dgd.dgd_q4_vocab_bytes(262144, 2816) == 262144 * 2816 // 64 * 40
+    assert dgd.dgd_q4_vocab_bytes(100, 96) == 128 * 2 * 64 * 40 // 64
+    for bad in [(0, 64), (1 << 25, 64), (64, 48), (64, 0), (64, 16)]:
+        assert dgd.dgd_q4_vocab_bytes(*bad) == 0, bad
+    f = lib.dgd_pack_vocab_q4
+    assert f(None, FAKE, FAKE, FAKE * 64, 64, 64, None) == dgd.DGD_EINVAL
+    assert f(FAKE, FAKE, FAKE, None, 64, 64, None) == dgd.DGD_EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE * 64, 64, 48, None) == dgd.DGD_EUNSUPPORTED
+    assert f(FAKE, FAKE, FAKE, FAKE * 64, 0, 64, None) == dgd.DGD_EUNSUPPORTED
+    assert f(FAKE + 4, FAKE, FAKE, FAKE * 64, 64, 64, None) == dgd.DGD_EINVAL   # codes misaligned
+    assert f(FAKE, FAKE + 1, FAKE, FAKE * 64, 64, 64, None) == dgd.DGD_EINVAL   # scales misaligned
+    assert f(FAKE, FAKE * 2, FAKE * 3, FAKE, 64, 64, None) == dgd.DGD_EINVAL    # output overlaps codes
     assert dgd.dgd_last_error()
 
 

@@ -18,8 +18,9 @@ import numpy as np
 import pytest
 
 from oracle import dgd_oracle as O
-from tests.parity import Report, compare_sc, compare_stats
-from uniform_state_discrete_step_amd.inputs import WORKLOADS, make_workload_arrays, shrink
+from tests.parity import Report, compare_sc, compare_stats, q4_device_table
+from uniform_state_discrete_step_amd.inputs import (WORKLOADS, make_workload_arrays, quantize_q4,
+                                                    shrink)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,6 +44,10 @@ class FullRun:
         if W is None:
             W, Hs = make_workload_arrays(wl, threads=16)
         self.W, self.Hs = W, Hs
+        if layout == dgd.DGD_VOCAB_Q4 and Wd is None:
+            # the GPU streams the 4-bit form; the oracle uses the table it stands for
+            Wd = q4_device_table(W, wl.V, wl.d, dev)
+            self.W = W = O.dequant_q4(*quantize_q4(W))
         if Wd is None:
             Wd = torch.from_numpy(W.view(np.int16)).to(dev)
             if layout == dgd.DGD_VOCAB_PACKED:
@@ -182,6 +187,13 @@ def test_gemma_vocab_full_run_with_lm_head_tail(dev):
     tail = O.Tail(norm_weight=make_norm_weight(wl.d, wl.cfg_seed), norm_eps=1e-6, softcap=30.0)
     _check(FullRun(wl, dev, tail=tail).run(sample_every=6, rows_per_canvas=6),
            f"{wl.name} with output norm and softcap")
+
+
+def test_gemma_vocab_full_run_q4_table(dev):
+    """The 4-bit table stream at the full size."""
+    wl = WORKLOADS["gemma_vocab"]
+    _check(FullRun(wl, dev, layout=2).run(sample_every=6, rows_per_canvas=6),
+           f"{wl.name} 4-bit table")
 
 
 def test_gemma_vocab_full_run_with_self_conditioning(dev):

@@ -276,6 +276,61 @@ def test_sc_embed_matches_the_oracle(dev, layout):
 
 
 # ----------------------------------------------------------------------------
+# 4-bit table
+# ----------------------------------------------------------------------------
+def test_q4_projection_is_exact_on_small_integers(dev):
+    """Scale 1 and minimum -8 give table values -8..7; with small-integer H
+    every fp32 partial sum is exact, so the logits must equal the integer
+    dot products bit for bit (catches any slip in the code, scale or
+    fragment layout of the 4-bit stream)."""
+    import torch
+    from uniform_state_discrete_step_amd import dgd
+    wl = shrink(WORKLOADS["tiny"], V=300, d=160, L=40, B=1, G=40, N=2)
+    rng = np.random.default_rng(17)
+    q = rng.integers(0, 16, size=(wl.V, wl.d)).astype(np.uint8)
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    sc = np.full((wl.V, wl.d // 32), 0x3F80, dtype=np.uint16)            # 1.0
+    mn = np.full((wl.V, wl.d // 32), 0xC100, dtype=np.uint16)            # -8.0
+    Hi = rng.integers(-2, 3, size=(wl.L, wl.d))
+    Hs = bf16(Hi).reshape(1, 1, 1, wl.L, wl.d).repeat(wl.N, axis=1)
+    Wq = dgd.pack_vocab_q4(torch.from_numpy(codes.reshape(-1)).to(dev),
+                           torch.from_numpy(sc.reshape(-1).view(np.int16)).to(dev),
+                           torch.from_numpy(mn.reshape(-1).view(np.int16)).to(dev), wl.V, wl.d)
+    ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev, logits=True,
+                      vocab_layout=dgd.DGD_VOCAB_Q4)
+    params = dgd.make_params(wl.N)
+    canvas = torch.zeros(wl.G, dtype=torch.int32, device=dev)
+    committed = torch.zeros(wl.G, dtype=torch.uint8, device=dev)
+    dgd.dgd_init_block(canvas, committed, 0, params, wl.seeds, ctx)
+    Hd = torch.from_numpy(Hs.view(np.int16)).to(dev)
+    dgd.dgd_step(Hd[0, 0].reshape(-1), Wq, canvas, committed, 0, 0, params, wl.seeds, ctx)
+    torch.cuda.synchronize()
+    z = ctx.logits.cpu().numpy().reshape(wl.L, wl.V).astype(np.float64)
+    ref = (Hi @ (q.astype(np.int64) - 8).T).astype(np.float64)
+    assert np.array_equal(z, ref)
+    # and the oracle's dequantized table is that integer table
+    assert np.array_equal(O.bf16_to_f64(O.dequant_q4(codes, sc, mn)), q.astype(np.float64) - 8)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(),                                               # tiny: V 1024, d 64
+    dict(V=1001, d=96, L=37, B=3, G=74, N=5),             # ragged rows, vocabulary, two blocks
+    dict(V=4096, d=160, L=70, B=2, G=70, N=4),            # a half-filled last chunk
+    dict(V=129, d=32, L=1, B=2, G=3, N=4),                # one group, one-position canvases
+], ids=["tiny", "ragged", "half_chunk", "one_group"])
+def test_q4_lockstep(dev, shape):
+    B = shape.get("B", 1)
+    wl = shrink(WORKLOADS["tiny"], name="q4", cfg_seed=19, seeds=tuple(range(B)),
+                bounds=tuple((0.1, 0.3, 0.05)[c % 3] for c in range(B)), **shape)
+    run_lockstep(wl, dev, layout=2)
+
+
+def test_q4_lockstep_with_tail_small_vocab(dev):
+    wl = WORKLOADS["small_vocab"]
+    run_lockstep(wl, dev, layout=2, tail=_tail(wl, softcap=30.0), steps=range(0, 48, 12))
+
+
+# ----------------------------------------------------------------------------
 # sparse label read
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("case", [

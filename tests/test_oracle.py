@@ -191,6 +191,14 @@ def test_round_bf16_agrees_with_the_float32_rounding():
     assert np.array_equal(O.round_bf16(x32.astype(np.float64)), f32_to_bf16_bits(x32))
 
 
+def test_the_two_bf16_roundings_agree_on_float32_values():
+    rng = np.random.default_rng(18)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-20, 20, 20000)).astype(np.float32)
+    ties = (np.arange(1, 2000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)   # exact halves
+    for v in (x, ties, -ties):
+        assert np.array_equal(O.round_bf16_f32(v), O.round_bf16(v.astype(np.float64)))
+
+
 def test_round_bf16_ties_to_even_and_rounds_once():
     one = 0x3F80
     assert O.round_bf16(np.array([1.0 + 2.0 ** -8]))[0] == one           # tie -> even (down)

@@ -610,6 +610,64 @@ constexpr uint32_t kPackChunkBytes = 8192;   // 4 steps x 2 fragments x 1 KB
 __host__ __device__ inline int packed_chunks(int d) { return (d + kKChunk - 1) / kKChunk; }
 __host__ __device__ inline int packed_groups(int V) { return (V + kPackRows - 1) / kPackRows; }
 
+// 4-bit table in streaming order.  Per 64-row group rg and 64-element hidden
+// chunk c, 2560 bytes:
+//   [0, 1024)     fragment f = 0: lane l, 16 bytes = four 32-bit words, word s
+//                 holding the codes of row 64 rg + l%32, hidden 64 c + 32 (l/32)
+//                 + 8 s + j in nibble j (j = 0..7)
+//   [1024, 2048)  the same for f = 1 (rows 64 rg + 32 + l%32)
+//   [2048, 2560)  lane l, 8 bytes: bf16 scale and minimum of (f = 0 row, group
+//                 2c + l/32), then of (f = 1 row, same group)
+// Rows past V and groups past d hold zero codes, scales and minima (value 0).
+constexpr uint32_t kQ4ChunkBytes = 2560;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+__global__ void __launch_bounds__(kThreads) k_pack_vocab_q4(const uint8_t* __restrict__ codes,
+                                                            const uint16_t* __restrict__ scales,
+                                                            const uint16_t* __restrict__ mins,
+                                                            uint8_t* __restrict__ out, int V, int d,
+                                                            int nk, int64_t units) {
+  const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;   // (rg, c, lane)
+  if (u >= units) return;
+  const int lane = (int)(u & 63);
+  const int64_t q = u >> 6;
+  const int c = (int)(q % nk);
+  const int64_t rg = q / nk;
+  const int h = lane >> 5, ngroups = d / 32;
+  const int grp = 2 * c + h;
+  uint8_t* blk = out + q * kQ4ChunkBytes;
+  uint32_t sm[2];
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    const int64_t v = rg * kPackRows + 32 * f + (lane & 31);
+    const bool ok = v < V && grp < ngroups;
+    u32x4_t w = {0u, 0u, 0u, 0u};
+    if (ok) {
+      const uint32_t* src = (const uint32_t*)(codes + v * (d / 2) + grp * 16);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) w[s] = src[s];
+    }
+    *(u32x4_t*)(blk + f * 1024 + lane * 16) = w;
+    sm[f] = ok ? ((uint32_t)scales[v * ngroups + grp] | ((uint32_t)mins[v * ngroups + grp] << 16)) : 0u;
+  }
+  *(u32x2_t*)(blk + 2048 + lane * 8) = u32x2_t{sm[0], sm[1]};
+}
+
+// One 32-bit word of a dequantized A fragment: elements 2e and 2e+1 of the
+// eight codes in `codes` (nibble j = element j), as bf16(fp32(s) q + fp32(m)).
+__device__ __forceinline__ uint32_t q4_pair(uint32_t codes, int e, float sc, float mn) {
+  // even elements in the low nibble of each byte, odd ones in the high: split
+  // once into two byte vectors (shared by the four words of a fragment) and
+  // convert byte e of each
+  const uint32_t lo = codes & 0x0F0F0F0Fu, hi = (codes >> 4) & 0x0F0F0F0Fu;
+  const float q0 = (float)((lo >> (8 * e)) & 0xFFu);
+  const float q1 = (float)((hi >> (8 * e)) & 0xFFu);
+  const float w0 = fmaf(sc, q0, mn), w1 = fmaf(sc, q1, mn);
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  const bf16x2_t p = {(__bf16)w0, (__bf16)w1};
+  return __builtin_bit_cast(uint32_t, p);
+}
+
 __global__ void __launch_bounds__(kThreads) k_pack_vocab(const uint16_t* __restrict__ W,
                                                          uint16_t* __restrict__ Wp, int V, int d,
                                                          int nk, int64_t units) {
@@ -646,7 +704,8 @@ __global__ void __launch_bounds__(kThreads) k_pack_vocab(const uint16_t* __restr
 //   * one barrier per chunk, inside MFMA step 3 (see chunk()).
 // The H stream is cyclic over the chunks, so a tile finds the first HB chunks
 // of H already in LDS.
-template <int NB, bool kLogits, bool kUniformKey, bool kCap, bool kTopK, int PW, int RING, int HB>
+template <int NB, bool kLogits, bool kUniformKey, bool kCap, bool kTopK, bool kQ4, int PW, int RING,
+          int HB>
 __global__ void __launch_bounds__(256 * PW) __attribute__((amdgpu_waves_per_eu(PW, PW)))
 k_project_packed(const ProjArgs a) {
   static_assert(NB == 1 || NB == 2 || NB == 4 || NB == 8, "NB");
@@ -665,7 +724,10 @@ k_project_packed(const ProjArgs a) {
   // the two W loads of that step 3, HB-2 whole chunks (8 W loads and HSEG
   // DMA loads each) and the six W loads of steps 0-2 of chunk c.  Tile
   // prologues only add loads after it, which keeps the wait sufficient.
-  constexpr int kDmaLag = 2 + (HB - 2) * (8 + HSEG) + 6;
+  // With the 4-bit table a chunk has three W loads, all issued at the end of
+  // step 3, so only those of that step 3 and of the HB-2 chunks between stay
+  // in flight.
+  constexpr int kDmaLag = kQ4 ? 3 + (HB - 2) * (3 + HSEG) : 2 + (HB - 2) * (8 + HSEG) + 6;
   static_assert(kDmaLag <= 63, "vmcnt range");
   __shared__ __attribute__((aligned(16))) uint8_t hsm[HB][HBUF];
   __shared__ __attribute__((aligned(16))) Rec recs[WAVES * PPW];
@@ -695,7 +757,8 @@ k_project_packed(const ProjArgs a) {
   const int nk = packed_chunks(a.d);
   const int nkr = (nk + RING - 1) / RING * RING;   // chunk loop padded to whole rings
   const size_t d = (size_t)a.d;
-  const uint32_t rg_bytes = (uint32_t)nk * kPackChunkBytes;
+  constexpr uint32_t kChunkBytes = kQ4 ? kQ4ChunkBytes : kPackChunkBytes;
+  const uint32_t rg_bytes = (uint32_t)nk * kChunkBytes;
   const int n_rg = packed_groups(a.V);
 
   // W fragments of the wave's 64-row group in tile vt (empty past the end)
@@ -756,99 +819,212 @@ k_project_packed(const ProjArgs a) {
     const int vbase = vt * kVocabTile + wv * kVocabPerWave;
     const __amdgpu_buffer_rsrc_t wr = wres_of(vt);
 
-    // W ring, first RING chunks of the tile, issued in chunk order (pinned:
-    // vmcnt retires in order, so waits for the first chunks need not drain
-    // the later ones)
-    u32x4_t ring[RING][8];
-#pragma unroll
-    for (int r = 0; r < RING; ++r) {
-      const uint32_t oob = (uint32_t)(r >= nk) << 31;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        __builtin_amdgcn_sched_barrier(0);
-        ring[r][j] = __builtin_amdgcn_raw_buffer_load_b128(
-            wr, ((uint32_t)r * kPackChunkBytes + lane_off + (uint32_t)j * 1024u) | oob, 0, kNonTemporal);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
     f32x16_t acc[kVB][NBW];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int vb = 0; vb < kVB; ++vb)
+      for (int vb = 0; vb < kVB; ++vb)
 #pragma unroll
-      for (int pb = 0; pb < NBW; ++pb)
+        for (int pb = 0; pb < NBW; ++pb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[vb][pb][i] = 0.f;
+          for (int i = 0; i < 16; ++i) acc[vb][pb][i] = 0.f;
+    };
+    if constexpr (kQ4) {
+      // 4-bit table: a chunk is two code vectors and the scales (three loads),
+      // so the ring is deeper for the same registers.  A fragments are
+      // dequantized one 32-bit word at a time between the MFMAs of the step
+      // before (two A buffers alternate by step parity), so the VALU work
+      // runs while the matrix pipe is busy.
+      u32x4_t qring[RING][2];
+      u32x2_t sring[RING];
+#pragma unroll
+      for (int r = 0; r < RING; ++r) {
+        const uint32_t oob = (uint32_t)(r >= nk) << 31;
+        const uint32_t base = (uint32_t)r * kQ4ChunkBytes;
+        __builtin_amdgcn_sched_barrier(0);
+        qring[r][0] = __builtin_amdgcn_raw_buffer_load_b128(wr, (base + lane_off) | oob, 0, kNonTemporal);
+        __builtin_amdgcn_sched_barrier(0);
+        qring[r][1] = __builtin_amdgcn_raw_buffer_load_b128(wr, (base + 1024u + lane_off) | oob, 0,
+                                                            kNonTemporal);
+        __builtin_amdgcn_sched_barrier(0);
+        sring[r] = __builtin_amdgcn_raw_buffer_load_b64(wr, (base + 2048u + (uint32_t)lane * 8u) | oob, 0,
+                                                        kNonTemporal);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      zero_acc();
+      u32x4_t abuf[2][2];   // [step parity][fragment f]: 8 bf16 each
+      // word k (0..7) of the A fragments of step s: fragment k / 4, word k % 4
+      auto deq_word = [&](const u32x4_t (&q)[2], const u32x2_t& sc, int s, int k, u32x4_t (&dst)[2]) {
+        const int f = k / 4, e = k % 4;
+        const uint32_t smw = sc[f];
+        dst[f][e] = q4_pair(q[f][s], e, __uint_as_float(smw << 16), __uint_as_float(smw & 0xffff0000u));
+      };
+#pragma unroll
+      for (int k = 0; k < 8; ++k) deq_word(qring[0], sring[0], 0, k, abuf[0]);
 
-    // One chunk c (LDS buffer hcur, W registers wreg).  Per MFMA step s the
-    // issue order is pinned by scheduling barriers: for each B fragment, its
-    // two MFMAs and then the LDS read of the same fragment of step s+1 into
-    // the register just consumed; then the two W loads of chunk c+RING into
-    // the W registers of step s.  Step 3 is split around the chunk's only
-    // barrier: the first half of its MFMAs, a wait for this wave's DMA of
-    // H(c+1) (kDmaLag later loads may stay in flight) and for its LDS reads,
-    // the barrier, then the reads of step 0 of chunk c+1 from hnext and the
-    // DMA of H(c+HB) into hcur (every wave has read its last fragment of
-    // chunk c before the barrier), then the rest.
-    auto chunk = [&](int c, u32x4_t (&wreg)[8], uint8_t* hcur, const uint8_t* hnext) {
-      const uint32_t woob = (uint32_t)(c + RING >= nk) << 31;
-      const uint32_t wbase = (uint32_t)(c + RING) * kPackChunkBytes + lane_off;
-      const int h2 = c + HB < nkr ? c + HB : c + HB - nkr;
-      const int hc2 = h2 < nk ? h2 : 0;   // any valid chunk for a padding one
-      auto mfma2 = [&](int s, int pb) {
-        const bf16x8_t a0 = as_bf16x8(wreg[2 * s]), a1 = as_bf16x8(wreg[2 * s + 1]);
-        acc[0][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfr[pb], acc[0][pb], 0, 0, 0);
-        acc[1][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bfr[pb], acc[1][pb], 0, 0, 0);
-      };
-      auto wload = [&](int s) {
-        wreg[2 * s] = __builtin_amdgcn_raw_buffer_load_b128(
-            wr, (wbase + (uint32_t)(2 * s) * 1024u) | woob, 0, kNonTemporal);
-        wreg[2 * s + 1] = __builtin_amdgcn_raw_buffer_load_b128(
-            wr, (wbase + (uint32_t)(2 * s + 1) * 1024u) | woob, 0, kNonTemporal);
-      };
+      auto chunk_q4 = [&](int c, u32x4_t (&qcur)[2], u32x2_t& scur, const u32x4_t (&qnext)[2],
+                          const u32x2_t& snext, uint8_t* hcur, const uint8_t* hnext) {
+        const uint32_t woob = (uint32_t)(c + RING >= nk) << 31;
+        const uint32_t wbase = (uint32_t)(c + RING) * kQ4ChunkBytes;
+        const int h2 = c + HB < nkr ? c + HB : c + HB - nkr;
+        const int hc2 = h2 < nk ? h2 : 0;
+        auto mfma2 = [&](int s, int pb) {
+          const bf16x8_t a0 = as_bf16x8(abuf[s & 1][0]), a1 = as_bf16x8(abuf[s & 1][1]);
+          acc[0][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfr[pb], acc[0][pb], 0, 0, 0);
+          acc[1][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bfr[pb], acc[1][pb], 0, 0, 0);
+        };
+        // the A word (pb) of the step after s: this chunk's codes, or the next
+        // chunk's step 0 during step 3
+        auto deq_next = [&](int s, int pb) {
+          if (pb >= 8) return;
+          if (s < 3) deq_word(qcur, scur, s + 1, pb, abuf[(s + 1) & 1]);
+          else deq_word(qnext, snext, 0, pb, abuf[0]);
+        };
 #pragma unroll
-      for (int s = 0; s < 3; ++s) {
+        for (int s = 0; s < 3; ++s) {
 #pragma unroll
-        for (int pb = 0; pb < NBW; ++pb) {
+          for (int pb = 0; pb < NBW; ++pb) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma2(s, pb);
+            __builtin_amdgcn_sched_barrier(0);
+            bfr[pb] = read_b(hcur, s + 1, pb);
+            deq_next(s, pb);
+            if constexpr (NBW < 8)
+              if (pb == NBW - 1)
+#pragma unroll
+                for (int k = NBW; k < 8; ++k) deq_next(s, k);
+          }
+        }
+#pragma unroll
+        for (int pb = 0; pb < NBW / 2; ++pb) {
           __builtin_amdgcn_sched_barrier(0);
-          mfma2(s, pb);
-          __builtin_amdgcn_sched_barrier(0);
-          bfr[pb] = read_b(hcur, s + 1, pb);
+          mfma2(3, pb);
         }
         __builtin_amdgcn_sched_barrier(0);
-        wload(s);
-      }
-#pragma unroll
-      for (int pb = 0; pb < NBW / 2; ++pb) {
+        __builtin_amdgcn_s_waitcnt(waitcnt_enc(kDmaLag, 0));
+        __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        mfma2(3, pb);
+#pragma unroll
+        for (int pb = 0; pb < NBW / 2; ++pb) bfr[pb] = read_b(hnext, 0, pb);
+        __builtin_amdgcn_sched_barrier(0);
+        dma_h(hc2, hcur);
+#pragma unroll
+        for (int pb = NBW / 2; pb < NBW; ++pb) {
+          __builtin_amdgcn_sched_barrier(0);
+          mfma2(3, pb);
+          __builtin_amdgcn_sched_barrier(0);
+          bfr[pb] = read_b(hnext, 0, pb);
+        }
+        // the next chunk's step-0 words, then the loads of chunk c + RING
+        // into the registers this chunk has finished with
+#pragma unroll
+        for (int k = 0; k < 8; ++k) deq_next(3, k);
+        __builtin_amdgcn_sched_barrier(0);
+        qcur[0] = __builtin_amdgcn_raw_buffer_load_b128(wr, (wbase + lane_off) | woob, 0, kNonTemporal);
+        __builtin_amdgcn_sched_barrier(0);
+        qcur[1] = __builtin_amdgcn_raw_buffer_load_b128(wr, (wbase + 1024u + lane_off) | woob, 0,
+                                                        kNonTemporal);
+        __builtin_amdgcn_sched_barrier(0);
+        scur = __builtin_amdgcn_raw_buffer_load_b64(wr, (wbase + 2048u + (uint32_t)lane * 8u) | woob, 0,
+                                                    kNonTemporal);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+#pragma unroll
+      for (int pb = 0; pb < NBW; ++pb) bfr[pb] = read_b(hsm[0], 0, pb);
+      for (int c = 0; c < nkr; c += RING) {
+#pragma unroll
+        for (int r = 0; r < RING; ++r)
+          chunk_q4(c + r, qring[r], sring[r], qring[(r + 1) % RING], sring[(r + 1) % RING],
+                   hsm[r % HB], hsm[(r + 1) % HB]);
+      }
+    } else {
+      // W ring, first RING chunks of the tile, issued in chunk order (pinned:
+      // vmcnt retires in order, so waits for the first chunks need not drain
+      // the later ones)
+      u32x4_t ring[RING][8];
+#pragma unroll
+      for (int r = 0; r < RING; ++r) {
+        const uint32_t oob = (uint32_t)(r >= nk) << 31;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          __builtin_amdgcn_sched_barrier(0);
+          ring[r][j] = __builtin_amdgcn_raw_buffer_load_b128(
+              wr, ((uint32_t)r * kPackChunkBytes + lane_off + (uint32_t)j * 1024u) | oob, 0, kNonTemporal);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_waitcnt(waitcnt_enc(kDmaLag, 0));
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
+      zero_acc();
+
+      // One chunk c (LDS buffer hcur, W registers wreg).  Per MFMA step s the
+      // issue order is pinned by scheduling barriers: for each B fragment, its
+      // two MFMAs and then the LDS read of the same fragment of step s+1 into
+      // the register just consumed; then the two W loads of chunk c+RING into
+      // the W registers of step s.  Step 3 is split around the chunk's only
+      // barrier: the first half of its MFMAs, a wait for this wave's DMA of
+      // H(c+1) (kDmaLag later loads may stay in flight) and for its LDS reads,
+      // the barrier, then the reads of step 0 of chunk c+1 from hnext and the
+      // DMA of H(c+HB) into hcur (every wave has read its last fragment of
+      // chunk c before the barrier), then the rest.
+      auto chunk = [&](int c, u32x4_t (&wreg)[8], uint8_t* hcur, const uint8_t* hnext) {
+        const uint32_t woob = (uint32_t)(c + RING >= nk) << 31;
+        const uint32_t wbase = (uint32_t)(c + RING) * kPackChunkBytes + lane_off;
+        const int h2 = c + HB < nkr ? c + HB : c + HB - nkr;
+        const int hc2 = h2 < nk ? h2 : 0;   // any valid chunk for a padding one
+        auto mfma2 = [&](int s, int pb) {
+          const bf16x8_t a0 = as_bf16x8(wreg[2 * s]), a1 = as_bf16x8(wreg[2 * s + 1]);
+          acc[0][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfr[pb], acc[0][pb], 0, 0, 0);
+          acc[1][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bfr[pb], acc[1][pb], 0, 0, 0);
+        };
+        auto wload = [&](int s) {
+          wreg[2 * s] = __builtin_amdgcn_raw_buffer_load_b128(
+              wr, (wbase + (uint32_t)(2 * s) * 1024u) | woob, 0, kNonTemporal);
+          wreg[2 * s + 1] = __builtin_amdgcn_raw_buffer_load_b128(
+              wr, (wbase + (uint32_t)(2 * s + 1) * 1024u) | woob, 0, kNonTemporal);
+        };
 #pragma unroll
-      for (int pb = 0; pb < NBW / 2; ++pb) bfr[pb] = read_b(hnext, 0, pb);
-      __builtin_amdgcn_sched_barrier(0);
-      dma_h(hc2, hcur);
+        for (int s = 0; s < 3; ++s) {
 #pragma unroll
-      for (int pb = NBW / 2; pb < NBW; ++pb) {
+          for (int pb = 0; pb < NBW; ++pb) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma2(s, pb);
+            __builtin_amdgcn_sched_barrier(0);
+            bfr[pb] = read_b(hcur, s + 1, pb);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          wload(s);
+        }
+#pragma unroll
+        for (int pb = 0; pb < NBW / 2; ++pb) {
+          __builtin_amdgcn_sched_barrier(0);
+          mfma2(3, pb);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        mfma2(3, pb);
+        __builtin_amdgcn_s_waitcnt(waitcnt_enc(kDmaLag, 0));
+        __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
-        bfr[pb] = read_b(hnext, 0, pb);
+#pragma unroll
+        for (int pb = 0; pb < NBW / 2; ++pb) bfr[pb] = read_b(hnext, 0, pb);
+        __builtin_amdgcn_sched_barrier(0);
+        dma_h(hc2, hcur);
+#pragma unroll
+        for (int pb = NBW / 2; pb < NBW; ++pb) {
+          __builtin_amdgcn_sched_barrier(0);
+          mfma2(3, pb);
+          __builtin_amdgcn_sched_barrier(0);
+          bfr[pb] = read_b(hnext, 0, pb);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wload(3);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // step-0 fragments of chunk 0 (H chunk 0 is in hsm[0]: loaded in the
+      // prologue or by the previous tile's stream, which waited for it)
+#pragma unroll
+      for (int pb = 0; pb < NBW; ++pb) bfr[pb] = read_b(hsm[0], 0, pb);
+      for (int c = 0; c < nkr; c += RING) {
+#pragma unroll
+        for (int r = 0; r < RING; ++r) chunk(c + r, ring[r], hsm[r % HB], hsm[(r + 1) % HB]);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      wload(3);
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // step-0 fragments of chunk 0 (H chunk 0 is in hsm[0]: loaded in the
-    // prologue or by the previous tile's stream, which waited for it)
-#pragma unroll
-    for (int pb = 0; pb < NBW; ++pb) bfr[pb] = read_b(hsm[0], 0, pb);
-    for (int c = 0; c < nkr; c += RING) {
-#pragma unroll
-      for (int r = 0; r < RING; ++r) chunk(c + r, ring[r], hsm[r % HB], hsm[(r + 1) % HB]);
+
     }
 
     // ---------------- epilogue: one position per lane per block ----------
@@ -1736,9 +1912,12 @@ int check_shape(const dgd_ctx* ctx) {
     return fail(DGD_EUNSUPPORTED, "d=%d must be a multiple of 8 in [8, %d]", ctx->d,
                 DGD_MAX_HIDDEN);
   if (!ctx->state) return fail(DGD_EINVAL, "ctx->state is NULL");
-  if (ctx->vocab_layout != DGD_VOCAB_ROWS && ctx->vocab_layout != DGD_VOCAB_PACKED)
-    return fail(DGD_EINVAL, "vocab_layout=%d is neither DGD_VOCAB_ROWS nor DGD_VOCAB_PACKED",
+  if (ctx->vocab_layout != DGD_VOCAB_ROWS && ctx->vocab_layout != DGD_VOCAB_PACKED &&
+      ctx->vocab_layout != DGD_VOCAB_Q4)
+    return fail(DGD_EINVAL, "vocab_layout=%d is not DGD_VOCAB_ROWS, DGD_VOCAB_PACKED or DGD_VOCAB_Q4",
                 ctx->vocab_layout);
+  if (ctx->vocab_layout == DGD_VOCAB_Q4 && ctx->d % 32 != 0)
+    return fail(DGD_EUNSUPPORTED, "d=%d: the 4-bit table needs a multiple of 32", ctx->d);
   return DGD_OK;
 }
 
@@ -1882,7 +2061,7 @@ void with_flags(F&& f, bool b, Rest... rest) {
 }
 
 struct Flags {
-  bool logits, uniform, cap, topk;
+  bool logits, uniform, cap, topk, q4;
 };
 
 template <int MB>
@@ -1900,14 +2079,22 @@ void launch_project_mb(const ProjArgs& a, dim3 grid, hipStream_t s, Flags fl) {
 // leads changed nothing or ran slower.)
 constexpr int kPackedPW = 1, kPackedRing = 2, kPackedHB = 2;
 
+// The 4-bit table keeps four chunks in its register ring (10 registers per
+// chunk against 32 for bf16 fragments).
+constexpr int kQ4Ring = 4;
+
 template <int NB>
 void launch_packed_nb(const ProjArgs& a, dim3 grid, hipStream_t s, Flags fl) {
-  constexpr int PW = kPackedPW, R = kPackedRing, HB = kPackedHB;
-  with_flags([&](auto lg, auto uni, auto cap, auto topk) {
-    hipLaunchKernelGGL((k_project_packed<NB, decltype(lg)::value, decltype(uni)::value,
-                                         decltype(cap)::value, decltype(topk)::value, PW, R, HB>),
-                       grid, dim3(256 * PW), 0, s, a);
-  }, fl.logits, fl.uniform, fl.cap, fl.topk);
+  constexpr int PW = kPackedPW, HB = kPackedHB;
+  with_flags([&](auto lg, auto uni, auto cap, auto topk, auto q4) {
+    constexpr bool kQ4 = decltype(q4)::value, kTopK = decltype(topk)::value;
+    constexpr int R = kQ4 ? kQ4Ring : kPackedRing;
+    // (the top-K recomputation reads bf16 fragments: never with a 4-bit table)
+    if constexpr (!(kQ4 && kTopK))
+      hipLaunchKernelGGL((k_project_packed<NB, decltype(lg)::value, decltype(uni)::value,
+                                           decltype(cap)::value, kTopK, kQ4, PW, R, HB>),
+                         grid, dim3(256 * PW), 0, s, a);
+  }, fl.logits, fl.uniform, fl.cap, fl.topk, fl.q4);
 }
 
 int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* committed,
@@ -1949,9 +2136,10 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   fill_keys(pa.key, seed, B);
   const bool topk = ctx->sc_topk > 0;
   if (topk) pa.cand = (ScEnt*)(ws + wl.cand);
-  const Flags fl{ctx->logits != nullptr, (L % 32) == 0, cap, topk};
+  const bool q4 = ctx->vocab_layout == DGD_VOCAB_Q4;
+  const Flags fl{ctx->logits != nullptr, (L % 32) == 0, cap, topk, q4};
   int rc;
-  if (ctx->vocab_layout == DGD_VOCAB_PACKED) {
+  if (ctx->vocab_layout == DGD_VOCAB_PACKED || ctx->vocab_layout == DGD_VOCAB_Q4) {
     const int NB = M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8;
     pa.n_mtiles = (M + 32 * NB - 1) / (32 * NB);
     const dim3 grid1(pa.n_mtiles * pa.P);
@@ -2109,6 +2297,36 @@ int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas, u
 size_t dgd_packed_vocab_bytes(int32_t V, int32_t d) {
   if (V < 1 || V > DGD_MAX_VOCAB || d < 8 || d > DGD_MAX_HIDDEN || d % 8 != 0) return 0;
   return (size_t)packed_groups(V) * kPackRows * (size_t)packed_chunks(d) * kKChunk * 2;
+}
+
+size_t dgd_q4_vocab_bytes(int32_t V, int32_t d) {
+  if (V < 1 || V > DGD_MAX_VOCAB || d < 32 || d > DGD_MAX_HIDDEN || d % 32 != 0) return 0;
+  return (size_t)packed_groups(V) * (size_t)packed_chunks(d) * kQ4ChunkBytes;
+}
+
+int dgd_pack_vocab_q4(const uint8_t* codes, const dgd_bf16* scales, const dgd_bf16* mins, void* W_q4,
+                      int32_t V, int32_t d, void* stream) {
+  g_err.clear();
+  if (!codes || !scales || !mins || !W_q4) return fail(DGD_EINVAL, "codes/scales/mins/W_q4 is NULL");
+  if (V < 1 || V > DGD_MAX_VOCAB) return fail(DGD_EUNSUPPORTED, "V=%d outside [1, 2^24]", V);
+  if (d < 32 || d > DGD_MAX_HIDDEN || d % 32 != 0)
+    return fail(DGD_EUNSUPPORTED, "d=%d must be a multiple of 32 in [32, %d]", d, DGD_MAX_HIDDEN);
+  if (((uintptr_t)codes & 15) || ((uintptr_t)scales & 1) || ((uintptr_t)mins & 1) || !aligned16(W_q4))
+    return fail(DGD_EINVAL, "codes/W_q4 must be 16-byte and scales/mins 2-byte aligned");
+  const size_t bytes = dgd_q4_vocab_bytes(V, d);
+  const uintptr_t o0 = (uintptr_t)W_q4, o1 = o0 + bytes;
+  const uintptr_t ranges[3][2] = {{(uintptr_t)codes, (uintptr_t)codes + (size_t)V * d / 2},
+                                  {(uintptr_t)scales, (uintptr_t)scales + (size_t)V * (d / 32) * 2},
+                                  {(uintptr_t)mins, (uintptr_t)mins + (size_t)V * (d / 32) * 2}};
+  for (const auto& r : ranges)
+    if (r[0] < o1 && o0 < r[1]) return fail(DGD_EINVAL, "W_q4 overlaps an input");
+  const int nk = packed_chunks(d);
+  const int64_t units = (int64_t)packed_groups(V) * nk * 64;
+  const int64_t blocks = (units + kThreads - 1) / kThreads;
+  hipLaunchKernelGGL(k_pack_vocab_q4, dim3((unsigned)blocks), dim3(kThreads), 0, (hipStream_t)stream,
+                     codes, scales, mins, (uint8_t*)W_q4, V, d, nk, units);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_pack_vocab_q4 launch");
 }
 
 int dgd_pack_vocab(const dgd_bf16* W_vocab, dgd_bf16* W_packed, int32_t V, int32_t d, void* stream) {

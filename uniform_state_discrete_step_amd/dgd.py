@@ -25,9 +25,11 @@ DGD_MAX_CANVAS_LEN = 4096
 
 DGD_VOCAB_ROWS = 0
 DGD_VOCAB_PACKED = 1
+DGD_VOCAB_Q4 = 2
 
 EXPORTED = ("dgd_state_bytes", "dgd_workspace_bytes", "dgd_init_block", "dgd_step", "dgd_run",
-            "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_sc_embed", "dgd_label_probs",
+            "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_q4_vocab_bytes", "dgd_pack_vocab_q4",
+            "dgd_sc_embed", "dgd_label_probs",
             "dgd_debug_gumbel",
             "dgd_last_error")
 
@@ -112,6 +114,12 @@ def load_library(path: str = LIB_PATH):
     lib.dgd_pack_vocab.restype = ctypes.c_int
     lib.dgd_pack_vocab.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                    ctypes.c_void_p]
+    lib.dgd_q4_vocab_bytes.restype = ctypes.c_size_t
+    lib.dgd_q4_vocab_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
+    lib.dgd_pack_vocab_q4.restype = ctypes.c_int
+    lib.dgd_pack_vocab_q4.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_void_p]
     lib.dgd_sc_embed.restype = ctypes.c_int
     lib.dgd_sc_embed.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -287,7 +295,8 @@ def dgd_init_block(canvas, committed, block, params: DgdParams, seeds, ctx: Cont
 def dgd_step(H, W_vocab, canvas, committed, block, step, params: DgdParams, seeds, ctx: Context,
              stream=None):
     c = ctx.as_ctypes(stream)
-    _check(load_library().dgd_step(_ptr(H, 2), _ptr(W_vocab, 2), _ptr(canvas, 4),
+    # (W_vocab: bf16 words, or the bytes of a 4-bit table: no element size)
+    _check(load_library().dgd_step(_ptr(H, 2), _ptr(W_vocab), _ptr(canvas, 4),
                                    _ptr(committed, 1), int(block), int(step),
                                    ctypes.byref(params), _seeds(seeds), ctypes.byref(c)))
 
@@ -295,7 +304,7 @@ def dgd_step(H, W_vocab, canvas, committed, block, step, params: DgdParams, seed
 def dgd_run(H_steps, W_vocab, canvas, committed, params: DgdParams, seeds, ctx: Context,
             stream=None):
     c = ctx.as_ctypes(stream)
-    _check(load_library().dgd_run(_ptr(H_steps, 2), _ptr(W_vocab, 2), _ptr(canvas, 4),
+    _check(load_library().dgd_run(_ptr(H_steps, 2), _ptr(W_vocab), _ptr(canvas, 4),
                                   _ptr(committed, 1), ctypes.byref(params), _seeds(seeds),
                                   ctypes.byref(c)))
 
@@ -314,6 +323,24 @@ def pack_vocab(W_vocab, V: int, d: int, stream=None):
     import torch
     out = torch.empty(dgd_packed_vocab_bytes(V, d) // 2, dtype=torch.int16, device=W_vocab.device)
     dgd_pack_vocab(W_vocab, out, V, d, stream)
+    return out
+
+
+def dgd_q4_vocab_bytes(V: int, d: int) -> int:
+    return int(load_library().dgd_q4_vocab_bytes(V, d))
+
+
+def dgd_pack_vocab_q4(codes, scales, mins, W_q4, V: int, d: int, stream=None):
+    _check(load_library().dgd_pack_vocab_q4(_ptr(codes, 1), _ptr(scales, 2), _ptr(mins, 2),
+                                            _ptr(W_q4, 1), int(V), int(d), _stream_handle(stream)))
+
+
+def pack_vocab_q4(codes, scales, mins, V: int, d: int, stream=None):
+    """Streaming form of a 4-bit table (a new uint8 device tensor) from device
+    tensors: codes uint8 [V*d/2], scales/mins int16 [V*d/32] (bf16 bits)."""
+    import torch
+    out = torch.empty(dgd_q4_vocab_bytes(V, d), dtype=torch.uint8, device=codes.device)
+    dgd_pack_vocab_q4(codes, scales, mins, out, V, d, stream)
     return out
 
 
