@@ -324,6 +324,16 @@ int dgd_pack_vocab(const dgd_bf16* W_vocab, dgd_bf16* W_packed, int32_t V, int32
  * natural-unit noise is out[i]*ln 2 - ln(ln 2).  Device float[n] output. */
 int dgd_debug_gumbel(const uint32_t* words, float* out, int64_t n, void* stream);
 
+/* Validation helper: Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel
+ * Random Numbers: As Easy as 1, 2, 3", SC'11) as the kernels compute it.
+ *   ctr  device uint32[n*4]: call i's counter (c0, c1, c2, c3), 16-byte aligned
+ *   key  device uint32[n*2]: call i's key (k0, k1), 8-byte aligned; or NULL to
+ *        use uniform_key (k0 = low word, k1 = high word) for every call, the
+ *        form the fused step runs with its key in scalar registers
+ *   out  device uint32[n*4]: the four output words, 16-byte aligned */
+int dgd_debug_philox(const uint32_t* ctr, const uint32_t* key, uint64_t uniform_key, uint32_t* out,
+                     int64_t n, void* stream);
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char* dgd_last_error(void);
 

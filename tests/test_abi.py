@@ -140,6 +140,12 @@ def test_invalid_step_block_and_pointers_are_refused(lib):
     assert lib.dgd_debug_gumbel(None, FAKE, 4, None) == dgd.DGD_EINVAL
     assert lib.dgd_debug_gumbel(FAKE, FAKE, -1, None) == dgd.DGD_EINVAL
     assert lib.dgd_debug_gumbel(FAKE, FAKE, 0, None) == dgd.DGD_OK
+    assert lib.dgd_debug_philox(None, None, 0, FAKE, 4, None) == dgd.DGD_EINVAL
+    assert lib.dgd_debug_philox(FAKE, None, 0, None, 4, None) == dgd.DGD_EINVAL
+    assert lib.dgd_debug_philox(FAKE, None, 0, FAKE, -1, None) == dgd.DGD_EINVAL
+    assert lib.dgd_debug_philox(FAKE + 4, None, 0, FAKE, 4, None) == dgd.DGD_EINVAL
+    assert lib.dgd_debug_philox(FAKE, FAKE + 4, 0, FAKE, 4, None) == dgd.DGD_EINVAL
+    assert lib.dgd_debug_philox(FAKE, None, 0, FAKE, 0, None) == dgd.DGD_OK
 
 
 @pytest.mark.parametrize("kw", [

@@ -70,6 +70,39 @@ def test_gumbel_transform_every_cell(dev):
     assert err.max() <= 2e-5
 
 
+@pytest.mark.parametrize("keyed", [True, False], ids=["per_call_keys", "uniform_key"])
+def test_philox_words_match_the_oracle(dev, keyed):
+    """The GPU generator against the oracle's separate implementation, bit
+    for bit, on 2^25 calls (1.3e8 words) with varied counters and keys."""
+    import torch
+    from uniform_state_discrete_step_amd import dgd
+    n = 1 << 25
+    rng = np.random.default_rng(20)
+    i = np.arange(n, dtype=np.uint64)
+    ctr = np.empty((n, 4), dtype=np.uint32)
+    ctr[:, 0] = i                                                    # every value of c0's range start
+    ctr[:, 1] = rng.integers(0, 1 << 32, n, dtype=np.uint64)
+    ctr[:, 2] = (i * 2654435761) >> 7
+    ctr[:, 3] = rng.integers(0, 4, n)                               # tags 0..3
+    key = rng.integers(0, 1 << 32, (n, 2), dtype=np.uint64).astype(np.uint32)
+    ukey = 0xFEEDFACE_0BADF00D
+    out = torch.empty(n * 4, dtype=torch.int32, device=dev)
+    dgd.dgd_debug_philox(torch.from_numpy(ctr.view(np.int32).reshape(-1)).to(dev),
+                         torch.from_numpy(key.view(np.int32).reshape(-1)).to(dev) if keyed else None,
+                         ukey, out)
+    torch.cuda.synchronize()
+    g = out.cpu().numpy().view(np.uint32).reshape(n, 4)
+    k0 = key[:, 0] if keyed else np.uint32(ukey & 0xFFFFFFFF)
+    k1 = key[:, 1] if keyed else np.uint32(ukey >> 32)
+    for a in range(0, n, 1 << 23):                                   # in slices: host memory
+        sl = slice(a, a + (1 << 23))
+        o = O.philox4x32_10(ctr[sl, 0], ctr[sl, 1], ctr[sl, 2], ctr[sl, 3],
+                            k0[sl] if keyed else k0, k1[sl] if keyed else k1)
+        for w in range(4):
+            bad = np.nonzero(g[sl, w] != o[w])[0]
+            assert bad.size == 0, f"word {w} differs at call {a + int(bad[0])}"
+
+
 def test_tiny_lockstep(dev, layout):
     run_lockstep(WORKLOADS["tiny"], dev, layout=layout)
 

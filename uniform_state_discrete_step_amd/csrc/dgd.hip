@@ -1833,6 +1833,24 @@ __global__ void k_debug_gumbel(const uint32_t* words, float* out, int64_t n) {
   if (i < n) out[i] = gumbel_bits(words[i]);
 }
 
+// The generator the kernels use, for validation: per-call keys (the
+// general form) or one key for all calls (the form whose key lives in scalar
+// registers, as the fused step uses it when a 32-row block is in one canvas).
+__global__ void k_debug_philox(const u32x4_t* ctr, const u32x2_t* key, uint32_t k0, uint32_t k1,
+                               u32x4_t* out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const u32x4_t c = ctr[i];
+  Philox4 p;
+  if (key) {
+    const u32x2_t k = key[i];
+    p = philox4x32_10(c[0], c[1], c[2], c[3], k[0], k[1]);
+  } else {
+    p = philox4x32_10_uniform_key(c[0], c[1], c[2], c[3], k0, k1);
+  }
+  out[i] = u32x4_t{p.x, p.y, p.z, p.w};
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -2402,6 +2420,23 @@ int dgd_label_probs(const dgd_bf16* H, int32_t rows, const dgd_bf16* W_vocab, in
   hipLaunchKernelGGL(k_label, dim3((unsigned)rows), dim3(kThreads), 0, (hipStream_t)stream, la);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? DGD_OK : hip_fail(e, "k_label launch");
+}
+
+int dgd_debug_philox(const uint32_t* ctr, const uint32_t* key, uint64_t uniform_key, uint32_t* out,
+                     int64_t n, void* stream) {
+  g_err.clear();
+  if (!ctr || !out) return fail(DGD_EINVAL, "ctr/out is NULL");
+  if (n < 0) return fail(DGD_EINVAL, "n < 0");
+  if (((uintptr_t)ctr & 15) || ((uintptr_t)out & 15) || ((uintptr_t)key & 7))
+    return fail(DGD_EINVAL, "ctr/out must be 16-byte and key 8-byte aligned");
+  if (n == 0) return DGD_OK;
+  const int64_t blocks = (n + 255) / 256;
+  if (blocks > 0x7fffffff) return fail(DGD_EUNSUPPORTED, "n too large");
+  hipLaunchKernelGGL(k_debug_philox, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4_t*)ctr, (const u32x2_t*)key, (uint32_t)(uniform_key & 0xffffffffu),
+                     (uint32_t)(uniform_key >> 32), (u32x4_t*)out, n);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_debug_philox launch");
 }
 
 int dgd_debug_gumbel(const uint32_t* words, float* out, int64_t n, void* stream) {

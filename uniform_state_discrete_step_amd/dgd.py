@@ -30,7 +30,7 @@ DGD_VOCAB_Q4 = 2
 EXPORTED = ("dgd_state_bytes", "dgd_workspace_bytes", "dgd_init_block", "dgd_step", "dgd_run",
             "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_q4_vocab_bytes", "dgd_pack_vocab_q4",
             "dgd_sc_embed", "dgd_label_probs",
-            "dgd_debug_gumbel",
+            "dgd_debug_philox", "dgd_debug_gumbel",
             "dgd_last_error")
 
 
@@ -130,6 +130,9 @@ def load_library(path: str = LIB_PATH):
                                     ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                     ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
+    lib.dgd_debug_philox.restype = ctypes.c_int
+    lib.dgd_debug_philox.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
+                                     ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.dgd_debug_gumbel.restype = ctypes.c_int
     lib.dgd_debug_gumbel.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                      ctypes.c_void_p]
@@ -360,6 +363,13 @@ def dgd_label_probs(H, rows: int, W_vocab, vocab_layout: int, V: int, d: int, la
                                           int(vocab_layout), int(V), int(d), arr, len(lab),
                                           float(temperature), float(softcap), _ptr(logits, 4),
                                           _ptr(probs, 4), _stream_handle(stream)))
+
+
+def dgd_debug_philox(ctr, key, uniform_key: int, out, stream=None):
+    """ctr int32 [n*4], key int32 [n*2] or None, out int32 [n*4] (device)."""
+    n = ctr.numel() // 4
+    _check(load_library().dgd_debug_philox(_ptr(ctr, 4), _ptr(key, 4), int(uniform_key),
+                                           _ptr(out, 4), n, _stream_handle(stream)))
 
 
 def dgd_debug_gumbel(words, out, stream=None):
