@@ -56,6 +56,38 @@ def measured_traffic(kernel):
     return rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
 
 
+def measured_ceilings(dgd, torch, table, dev):
+    """What this GPU sustains on the projection's two resources: a streaming
+    read of the table the step reads (HBM), and independent bf16 MFMAs on
+    operands taken from it (one wave per SIMD).  Best of 5 runs each."""
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    nbytes = table.numel() * table.element_size()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    dgd.dgd_ceiling_hbm_read(table, nbytes, sink)
+    best = float("inf")
+    for _ in range(5):
+        e0.record()
+        dgd.dgd_ceiling_hbm_read(table, nbytes, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    hbm = nbytes / best / 1e9
+    wgs, rounds = 256, 3000
+    fsink = torch.empty(wgs * 256, dtype=torch.float32, device=dev)
+    dgd.dgd_ceiling_mfma_bf16(table, min(nbytes, 1 << 26), rounds, wgs, fsink)
+    best = float("inf")
+    for _ in range(5):
+        e0.record()
+        dgd.dgd_ceiling_mfma_bf16(table, min(nbytes, 1 << 26), rounds, wgs, fsink)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    mfma = wgs * 4 * rounds * 64 * 32768.0 / best / 1e12
+    return {"hbm_read_GBs": hbm, "mfma_bf16_TFLOPs": mfma,
+            "how": "streaming 16-byte reads of the step's table (best of 5); "
+                   "v_mfma_f32_32x32x16_bf16 on operands from the table, one wave per SIMD (best of 5)"}
+
+
 def cpu_baseline(wl, W, Hs, tail=None, sc_topk=0):
     """Time the oracle (as it stands) on a few full steps of the workload."""
     from oracle import dgd_oracle as O
@@ -242,6 +274,9 @@ def main():
              "frac": hbm_frac} if bound == "hbm" else
             {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": mfma_frac})
+    ceil = measured_ceilings(dgd, torch, Wd, dev)
+    log(f"[bench] measured ceilings: HBM read {ceil['hbm_read_GBs']:.0f} GB/s, "
+        f"MFMA bf16 {ceil['mfma_bf16_TFLOPs']:.0f} TFLOP/s")
     kname = "k_project" if layout == dgd.DGD_VOCAB_ROWS else "k_project_packed"
     traffic = (measured_traffic(kname)
                if wl.name == "gemma_vocab" and not args.lm_head_tail and not args.sc_topk
@@ -251,7 +286,11 @@ def main():
                  "kernel_launches": k1_n, "algorithmic_bytes_per_launch": alg_bytes,
                  "flops_per_launch": flops,
                  "other": {"hbm_GBs": gbs, "hbm_frac": hbm_frac, "mfma_TFLOPs": tflops,
-                           "mfma_frac": mfma_frac}})
+                           "mfma_frac": mfma_frac},
+                 "measured_ceilings": ceil,
+                 "frac_of_measured_ceiling": {
+                     "hbm": gbs / ceil["hbm_read_GBs"],
+                     "mfma": tflops / ceil["mfma_bf16_TFLOPs"]}})
 
     steps_per_s = args.steps / (ms * 1e-3)
     out = {

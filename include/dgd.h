@@ -334,6 +334,20 @@ int dgd_debug_gumbel(const uint32_t* words, float* out, int64_t n, void* stream)
 int dgd_debug_philox(const uint32_t* ctr, const uint32_t* key, uint64_t uniform_key, uint32_t* out,
                      int64_t n, void* stream);
 
+/* Measurement helpers (not part of the step): what this GPU sustains on the
+ * two resources the projection uses, for reports against measured ceilings
+ * beside the published peaks.  The caller times them (e.g. with events).
+ * dgd_ceiling_hbm_read: reads `bytes` (a multiple of 16) of device memory at
+ *   `buf` once, 16-byte non-temporal loads from 4096 workgroups, folding
+ *   them into sink (device uint32[1024], XOR-accumulated: clear it first).
+ * dgd_ceiling_mfma_bf16: `workgroups` workgroups of 4 waves (one per SIMD),
+ *   each wave `rounds` x 64 independent v_mfma_f32_32x32x16_bf16 (32768 flop
+ *   each) on operands read once from `ops` (device, `bytes` >= 256); writes
+ *   device float[workgroups*256] to sink. */
+int dgd_ceiling_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+int dgd_ceiling_mfma_bf16(const void* ops, size_t bytes, int64_t rounds, int32_t workgroups, float* sink,
+                          void* stream);
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char* dgd_last_error(void);
 

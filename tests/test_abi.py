@@ -146,6 +146,14 @@ def test_invalid_step_block_and_pointers_are_refused(lib):
     assert lib.dgd_debug_philox(FAKE + 4, None, 0, FAKE, 4, None) == dgd.DGD_EINVAL
     assert lib.dgd_debug_philox(FAKE, FAKE + 4, 0, FAKE, 4, None) == dgd.DGD_EINVAL
     assert lib.dgd_debug_philox(FAKE, None, 0, FAKE, 0, None) == dgd.DGD_OK
+    assert lib.dgd_ceiling_hbm_read(None, 64, FAKE, None) == dgd.DGD_EINVAL
+    assert lib.dgd_ceiling_hbm_read(FAKE, 60, FAKE, None) == dgd.DGD_EINVAL
+    assert lib.dgd_ceiling_hbm_read(FAKE + 8, 64, FAKE, None) == dgd.DGD_EINVAL
+    assert lib.dgd_ceiling_hbm_read(FAKE, 0, FAKE, None) == dgd.DGD_OK
+    assert lib.dgd_ceiling_mfma_bf16(FAKE, 128, 1, 1, FAKE, None) == dgd.DGD_EINVAL   # < 256 bytes
+    assert lib.dgd_ceiling_mfma_bf16(FAKE, 4096, 0, 1, FAKE, None) == dgd.DGD_EINVAL
+    assert lib.dgd_ceiling_mfma_bf16(FAKE, 4096, 1, 0, FAKE, None) == dgd.DGD_EINVAL
+    assert lib.dgd_ceiling_mfma_bf16(None, 4096, 1, 1, FAKE, None) == dgd.DGD_EINVAL
 
 
 @pytest.mark.parametrize("kw", [

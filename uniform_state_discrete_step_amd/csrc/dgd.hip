@@ -1852,6 +1852,63 @@ __global__ void k_debug_philox(const u32x4_t* ctr, const u32x2_t* key, uint32_t 
 }
 
 // ---------------------------------------------------------------------------
+// Ceilings: what this GPU sustains on the projection's two resources
+// ---------------------------------------------------------------------------
+// HBM: every thread streams 16-byte non-temporal loads over the buffer, four
+// in flight, and folds them with XOR into one word per workgroup.
+__global__ void __launch_bounds__(256) k_ceiling_hbm(const u32x4_t* __restrict__ buf, int64_t n16,
+                                                     uint32_t* sink) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t x = 0;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    u32x4_t v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __builtin_nontemporal_load(buf + i + k * stride);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) x ^= v[k][0] ^ v[k][1] ^ v[k][2] ^ v[k][3];
+  }
+  for (; i < n16; i += stride) {
+    const u32x4_t v = __builtin_nontemporal_load(buf + i);
+    x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x ^= __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink + blockIdx.x % 1024, x);
+}
+
+// MFMA: one wave per SIMD, eight A and eight B fragments of real data in
+// registers (from `ops`), every (A, B) pair per round into eight
+// accumulators: 64 independent v_mfma_f32_32x32x16_bf16 per round.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_ceiling_mfma(const u32x4_t* __restrict__ ops, int64_t n16, int64_t rounds, float* sink) {
+  const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
+  bf16x8_t a[8], b[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    a[k] = as_bf16x8(ops[(base + k) % n16]);
+    b[k] = as_bf16x8(ops[(base + 8 + k) % n16]);
+  }
+  f32x16_t acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+  for (int64_t r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[j], 0, 0, 0);
+  }
+  float t = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t += acc[j][e];
+  sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = t;
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 thread_local std::string g_err;
@@ -2437,6 +2494,31 @@ int dgd_debug_philox(const uint32_t* ctr, const uint32_t* key, uint64_t uniform_
                      (uint32_t)(uniform_key >> 32), (u32x4_t*)out, n);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? DGD_OK : hip_fail(e, "k_debug_philox launch");
+}
+
+int dgd_ceiling_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  g_err.clear();
+  if (!buf || !sink) return fail(DGD_EINVAL, "buf/sink is NULL");
+  if (!aligned16(buf) || bytes % 16 != 0) return fail(DGD_EINVAL, "buf must be 16-byte aligned, bytes a multiple of 16");
+  if (bytes == 0) return DGD_OK;
+  hipLaunchKernelGGL(k_ceiling_hbm, dim3(4096), dim3(256), 0, (hipStream_t)stream, (const u32x4_t*)buf,
+                     (int64_t)(bytes / 16), sink);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_ceiling_hbm launch");
+}
+
+int dgd_ceiling_mfma_bf16(const void* ops, size_t bytes, int64_t rounds, int32_t workgroups, float* sink,
+                          void* stream) {
+  g_err.clear();
+  if (!ops || !sink) return fail(DGD_EINVAL, "ops/sink is NULL");
+  if (!aligned16(ops) || bytes < 256 || bytes % 16 != 0)
+    return fail(DGD_EINVAL, "ops must be 16-byte aligned, bytes >= 256 and a multiple of 16");
+  if (rounds < 1 || workgroups < 1 || workgroups > (1 << 20))
+    return fail(DGD_EINVAL, "rounds >= 1 and workgroups in [1, 2^20] required");
+  hipLaunchKernelGGL(k_ceiling_mfma, dim3((unsigned)workgroups), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4_t*)ops, (int64_t)(bytes / 16), rounds, sink);
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_ceiling_mfma launch");
 }
 
 int dgd_debug_gumbel(const uint32_t* words, float* out, int64_t n, void* stream) {

@@ -30,7 +30,8 @@ DGD_VOCAB_Q4 = 2
 EXPORTED = ("dgd_state_bytes", "dgd_workspace_bytes", "dgd_init_block", "dgd_step", "dgd_run",
             "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_q4_vocab_bytes", "dgd_pack_vocab_q4",
             "dgd_sc_embed", "dgd_label_probs",
-            "dgd_debug_philox", "dgd_debug_gumbel",
+            "dgd_ceiling_hbm_read", "dgd_ceiling_mfma_bf16", "dgd_debug_philox",
+            "dgd_debug_gumbel",
             "dgd_last_error")
 
 
@@ -130,6 +131,12 @@ def load_library(path: str = LIB_PATH):
                                     ctypes.POINTER(ctypes.c_int32), ctypes.c_int32,
                                     ctypes.c_float, ctypes.c_float, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p]
+    lib.dgd_ceiling_hbm_read.restype = ctypes.c_int
+    lib.dgd_ceiling_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                         ctypes.c_void_p]
+    lib.dgd_ceiling_mfma_bf16.restype = ctypes.c_int
+    lib.dgd_ceiling_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64,
+                                          ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.dgd_debug_philox.restype = ctypes.c_int
     lib.dgd_debug_philox.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_uint64,
                                      ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
@@ -363,6 +370,17 @@ def dgd_label_probs(H, rows: int, W_vocab, vocab_layout: int, V: int, d: int, la
                                           int(vocab_layout), int(V), int(d), arr, len(lab),
                                           float(temperature), float(softcap), _ptr(logits, 4),
                                           _ptr(probs, 4), _stream_handle(stream)))
+
+
+def dgd_ceiling_hbm_read(buf, nbytes: int, sink, stream=None):
+    _check(load_library().dgd_ceiling_hbm_read(_ptr(buf), int(nbytes), _ptr(sink, 4),
+                                               _stream_handle(stream)))
+
+
+def dgd_ceiling_mfma_bf16(ops, nbytes: int, rounds: int, workgroups: int, sink, stream=None):
+    _check(load_library().dgd_ceiling_mfma_bf16(_ptr(ops), int(nbytes), int(rounds),
+                                                int(workgroups), _ptr(sink, 4),
+                                                _stream_handle(stream)))
 
 
 def dgd_debug_philox(ctr, key, uniform_key: int, out, stream=None):
