@@ -373,3 +373,48 @@ class Lockstep:
                 if all(s.done for s in self.states):
                     break
         return rep
+
+
+def free_running(ls: Lockstep, rep: Report = None):
+    """Both sides run the whole generation on their own state, no state is
+    pushed.  After every step the GPU's canvas, committed mask and done flags
+    must equal the oracle's.  At the first step where they differ, both
+    started from the same state, so that step is compared as a lockstep step:
+    it must show a counted band event and no failure; the runs then part
+    legitimately and the comparison stops.  Returns (rep, first divergence or
+    None)."""
+    torch, wl, dgd = ls.torch, ls.wl, ls.dgd
+    rep = rep or Report()
+    states = [O.new_state(wl.G, wl.L) for _ in range(wl.B)]
+    for b in range(wl.blocks):
+        states = [O.init_block(st, b, wl.L, wl.V, wl.seeds[c]) for c, st in enumerate(states)]
+        dgd.dgd_init_block(ls.canvas, ls.committed, b, ls.params, wl.seeds, ls.ctx)
+        for s_idx in range(wl.N):
+            dgd.dgd_step(ls.Hd[b, s_idx].reshape(-1), ls.Wd, ls.canvas, ls.committed, b, s_idx,
+                         ls.params, wl.seeds, ls.ctx)
+            torch.cuda.synchronize()
+            for c in range(wl.B):
+                before = states[c]
+                after, info = O.step(before, ls.Hs[b, s_idx, c], ls.W, b, s_idx, ls.P,
+                                     wl.seeds[c], wl.bounds[c], W64=ls.W64, tail=ls.tail)
+                g = ls.pull(c)
+                same = (np.array_equal(g["canvas"], after.canvas)
+                        and np.array_equal(g["committed"], after.committed)
+                        and bool(g["done"]) == bool(after.done))
+                if not same:
+                    n_before = rep.argmax_band + rep.sample_band + rep.commit_band + rep.conv_band
+                    compare_step(rep, f"free run: block {b} step {s_idx} canvas {c}", before, after,
+                                 info, g, wl.L, wl.V, b, s_idx, ls.P, wl.seeds[c],
+                                 float(np.float32(wl.bounds[c])))
+                    n_after = rep.argmax_band + rep.sample_band + rep.commit_band + rep.conv_band
+                    if n_after == n_before:
+                        rep.fail(f"free run: block {b} step {s_idx} canvas {c} parts from the oracle "
+                                 f"without a band event")
+                    return rep, (b, s_idx, c)
+                if not info.get("skipped"):
+                    rep.steps += 1
+                    rep.positions += wl.L
+                states[c] = after
+            if all(st.done for st in states):
+                break
+    return rep, None

@@ -103,6 +103,24 @@ def test_philox_words_match_the_oracle(dev, keyed):
             assert bad.size == 0, f"word {w} differs at call {a + int(bad[0])}"
 
 
+@pytest.mark.parametrize("name,shape", [
+    ("tiny", {}),
+    ("tiny", dict(B=3, G=32, seeds=(0, 1, 2**63 + 5), bounds=(0.1, 0.0, 1.0))),
+    ("tiny", dict(V=1001, d=72, L=37, B=3, G=74, N=5, seeds=(4, 5, 6), bounds=(0.1, 0.3, 0.05))),
+    ("small_vocab", {}),
+], ids=["tiny", "tiny_batched", "ragged", "small_vocab"])
+def test_free_running_generation_matches_the_oracle(dev, name, shape):
+    """End to end: whole generations on both sides from their own state."""
+    from tests.parity import free_running
+    wl = shrink(WORKLOADS[name], **shape) if shape else WORKLOADS[name]
+    W, Hs = make_workload_arrays(wl, threads=8)
+    ls = Lockstep(wl, W, Hs, dev, layout=1)
+    rep, div = free_running(ls)
+    print(f"\n[free run {name}] {rep.summary()} first divergence: {div}", flush=True)
+    assert not rep.failures, "\n".join(rep.failures)
+    assert rep.steps > 0
+
+
 def test_tiny_lockstep(dev, layout):
     run_lockstep(WORKLOADS["tiny"], dev, layout=layout)
 
