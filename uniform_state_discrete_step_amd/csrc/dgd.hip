@@ -42,6 +42,14 @@ namespace {
 // tiling constants of the projection
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 256;           // merge/commit and init kernels: 4 waves of 64
+
+// Blocks of 32 positions per epilogue loop body of the packed projection
+// (four: the accumulator rotation between bodies then moves 256 instead of
+// 1792 registers per tile, 14 us less at 256 x 262144 x 2816; the variant
+// that also keeps top-K lists runs out of registers with four and uses one)
+#ifndef DGD_EPI_UNROLL
+#define DGD_EPI_UNROLL 4
+#endif
 constexpr int kWaves = kThreads / 64;
 constexpr int kPThreads = 512;          // projection: 8 waves, two per SIMD
 constexpr int kVGroups = 4;             // projection waves along the vocabulary ...
@@ -1028,48 +1036,57 @@ k_project_packed(const ProjArgs a) {
     }
 
     // ---------------- epilogue: one position per lane per block ----------
-    // One loop body for all blocks (not unrolled: it is long).  Block pb is
-    // always taken from acc[.][0] and the accumulators are rotated down one
-    // block at the end of the body, so every register index stays static and
-    // the accumulators never leave AGPRs.
+    // One loop body for EU blocks at a time (the body is long, so the loop
+    // is not unrolled further).  Body block u is always taken from acc[.][u]
+    // and the accumulators are rotated down EU blocks at the end of the body,
+    // so every register index stays static and the accumulators never leave
+    // AGPRs.
+    constexpr int EU0 = kTopK ? 1 : DGD_EPI_UNROLL;
+    constexpr int EU = NBW < EU0 ? NBW : EU0;
+    static_assert(NBW % EU == 0, "epilogue unroll");
 #pragma unroll 1
-    for (int pb = 0; pb < NBW; ++pb) {
-      f32x16_t z[kVB];
+    for (int pb0 = 0; pb0 < NBW; pb0 += EU) {
 #pragma unroll
-      for (int vb = 0; vb < kVB; ++vb) z[vb] = acc[vb][0];
-      const int r = row0 + wp * PPW + pb * 32 + col;
-      const bool rvalid = r < a.M;
-      int cv = rvalid ? r / a.L : 0;
-      if constexpr (kUniformKey) cv = __builtin_amdgcn_readfirstlane(cv);
-      const int p = r - cv * a.L;
-      const uint32_t pabs = (uint32_t)(a.block * a.L + p);
-      const uint32_t key0 = a.key[cv][0], key1 = a.key[cv][1];
+      for (int u = 0; u < EU; ++u) {
+        const int pb = pb0 + u;
+        f32x16_t z[kVB];
+#pragma unroll
+        for (int vb = 0; vb < kVB; ++vb) z[vb] = acc[vb][u];
+        const int r = row0 + wp * PPW + pb * 32 + col;
+        const bool rvalid = r < a.M;
+        int cv = rvalid ? r / a.L : 0;
+        if constexpr (kUniformKey) cv = __builtin_amdgcn_readfirstlane(cv);
+        const int p = r - cv * a.L;
+        const uint32_t pabs = (uint32_t)(a.block * a.L + p);
+        const uint32_t key0 = a.key[cv][0], key1 = a.key[cv][1];
 
-      if constexpr (kLogits) {
-        if (rvalid) {
+        if constexpr (kLogits) {
+          if (rvalid) {
 #pragma unroll
-          for (int vb = 0; vb < kVB; ++vb)
+            for (int vb = 0; vb < kVB; ++vb)
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int v0 = vbase + vb * 32 + 8 * q + 4 * half;
-              float* dst = a.logits + (size_t)r * a.V + v0;
+              for (int q = 0; q < 4; ++q) {
+                const int v0 = vbase + vb * 32 + 8 * q + 4 * half;
+                float* dst = a.logits + (size_t)r * a.V + v0;
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (v0 + e < a.V) dst[e] = z[vb][4 * q + e];
-            }
+                for (int e = 0; e < 4; ++e)
+                  if (v0 + e < a.V) dst[e] = z[vb][4 * q + e];
+              }
+          }
         }
+        const Rec wrec = tile_record<kUniformKey, kCap>(z, vbase, half, a.V, a.c2, a.cap_in, a.cap_out,
+                                                        pabs, (uint32_t)a.gstep, key0, key1);
+        if (half == 0) {
+          Rec* slot = recs + wave * PPW + pb * 32 + col;
+          rec_store(slot, rec_merge(rec_load(slot), wrec));
+        }
+        if constexpr (kTopK) sc_tile_update(z, vbase, half, slist + (wave * PPW + pb * 32 + col) * kScWave);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const Rec wrec = tile_record<kUniformKey, kCap>(z, vbase, half, a.V, a.c2, a.cap_in, a.cap_out, pabs,
-                                                      (uint32_t)a.gstep, key0, key1);
-      if (half == 0) {
-        Rec* slot = recs + wave * PPW + pb * 32 + col;
-        rec_store(slot, rec_merge(rec_load(slot), wrec));
-      }
-      if constexpr (kTopK) sc_tile_update(z, vbase, half, slist + (wave * PPW + pb * 32 + col) * kScWave);
 #pragma unroll
       for (int vb = 0; vb < kVB; ++vb)
 #pragma unroll
-        for (int k = 0; k + 1 < NBW; ++k) acc[vb][k] = acc[vb][k + 1];
+        for (int k = 0; k + EU < NBW; ++k) acc[vb][k] = acc[vb][k + EU];
     }
   }
 
