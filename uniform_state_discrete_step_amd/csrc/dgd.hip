@@ -542,20 +542,14 @@ k_project(const ProjArgs a) {
     }
 
     // ---------------- epilogue: one position per lane per block ----------
-    // One loop body for all blocks (not unrolled: it is long); the switch
-    // keeps every accumulator index static so the tile stays in registers.
+    // One loop body for all blocks (not unrolled: it is long).  Block pb is
+    // always taken from acc[.][0] and the accumulators are rotated down one
+    // block at the end of the body, so every register index stays static.
 #pragma unroll 1
     for (int pb = 0; pb < MBW; ++pb) {
       f32x16_t z[kVB];
-      switch (pb) {
-#define DGD_TAKE(P)                                            \
-  case P:                                                      \
-    _Pragma("unroll") for (int vb = 0; vb < kVB; ++vb)         \
-        z[vb] = acc[vb][(P) < MBW ? (P) : 0];                  \
-    break;
-        DGD_TAKE(0) DGD_TAKE(1) DGD_TAKE(2) DGD_TAKE(3)
-#undef DGD_TAKE
-      }
+#pragma unroll
+      for (int vb = 0; vb < kVB; ++vb) z[vb] = acc[vb][0];
       const int r = row0 + wp * PPW + pb * 32 + col;
       const bool rvalid = r < a.M;
       int cv = rvalid ? r / a.L : 0;
@@ -585,6 +579,10 @@ k_project(const ProjArgs a) {
         Rec* slot = recs + wave * PPW + pb * 32 + col;
         rec_store(slot, rec_merge(rec_load(slot), wrec));
       }
+#pragma unroll
+      for (int vb = 0; vb < kVB; ++vb)
+#pragma unroll
+        for (int k = 0; k + 1 < MBW; ++k) acc[vb][k] = acc[vb][k + 1];
     }
   }
 
