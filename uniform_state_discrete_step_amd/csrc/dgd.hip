@@ -13,8 +13,16 @@
 //                   sorts the open positions by entropy, applies the entropy
 //                   bound, writes samples and re-noises the rest.
 // plus k_init_block at the start of each block, and, when the caller asks for
-// the lm-head tail, k_rmsnorm (the output norm, before the projection) and a
-// softcap applied to the logits inside the projection's epilogue.
+// them:
+//   k_rmsnorm       the output norm of H, before the projection (the logit
+//                   softcap is applied inside the projection's epilogue);
+//   k_sc_topk       the self-conditioning top-K of every position, from
+//                   candidate lists the projection's epilogue keeps;
+//   k_sc_embed      the next forward's self-conditioning input from a top-K;
+//   k_label         the sparse label read for typed decisions.
+// Tables: k_pack_vocab (bf16, streaming order) and k_pack_vocab_q4 (4-bit).
+// Validation and measurement: k_debug_gumbel, k_debug_philox, k_ceiling_hbm,
+// k_ceiling_mfma.
 //
 // The method follows "The Annotated DiffusionGemma" walkthrough, section
 // "Sampling" (temperature, entropy, low-entropy prefix, early stop), with the
@@ -1280,8 +1288,6 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
   for (int p = tid; p < L; p += kThreads) a.st_prev[rbase + p] = a.rowA[rbase + p];
 }
 
-// Grid (ceil(L/4), B); one wave per position merges that position's partial
-// records (fixed order: lanes over the groups, then a butterfly).
 // ---------------------------------------------------------------------------
 // k_rmsnorm: the output norm of the final hidden states
 // ---------------------------------------------------------------------------
@@ -1354,6 +1360,8 @@ __global__ void __launch_bounds__(kThreads) k_rmsnorm(const uint16_t* __restrict
   }
 }
 
+// Grid (ceil(L/4), B); one wave per position merges that position's partial
+// records (fixed order: lanes over the groups, then a butterfly).
 __global__ void __launch_bounds__(kThreads) k_merge(const CommitArgs a) {
   const int c = blockIdx.y;
   if (a.st_done[c]) return;
