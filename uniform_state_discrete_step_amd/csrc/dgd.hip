@@ -2181,6 +2181,10 @@ constexpr int kPackedPW = 1, kPackedRing = 2, kPackedHB = 2;
 // chunk against 32 for bf16 fragments).
 constexpr int kQ4Ring = 4;
 
+// Workgroups that fill MI355X's 256 compute units once (the packed
+// projection runs one workgroup per CU).
+constexpr int kFillWorkgroups = 256;
+
 template <int NB>
 void launch_packed_nb(const ProjArgs& a, dim3 grid, hipStream_t s, Flags fl) {
   constexpr int PW = kPackedPW, HB = kPackedHB;
@@ -2238,7 +2242,11 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   const Flags fl{ctx->logits != nullptr, (L % 32) == 0, cap, topk, q4};
   int rc;
   if (ctx->vocab_layout == DGD_VOCAB_PACKED || ctx->vocab_layout == DGD_VOCAB_Q4) {
-    const int NB = M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8;
+    int NB = M <= 32 ? 1 : M <= 64 ? 2 : M <= 128 ? 4 : 8;
+    // A small vocabulary leaves CUs idle (one workgroup per tile and group):
+    // split the positions into more tiles until the grid covers every CU.
+    // Each (position, group) record is computed the same way in any tiling.
+    while (NB > 1 && ((M + 32 * NB - 1) / (32 * NB)) * wl.P < kFillWorkgroups) NB >>= 1;
     pa.n_mtiles = (M + 32 * NB - 1) / (32 * NB);
     const dim3 grid1(pa.n_mtiles * pa.P);
     if ((rc = timer.begin(stream))) return rc;
