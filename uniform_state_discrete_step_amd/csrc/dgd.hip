@@ -1144,10 +1144,10 @@ __device__ inline int block_sum_i32(int v, int* red) {
 __device__ void commit_canvas(const CommitArgs& a, int c) {
   __shared__ unsigned long long keys[DGD_MAX_CANVAS_LEN];    // (entropy bits, position)
   __shared__ unsigned long long ranked[DGD_MAX_CANVAS_LEN];  // eligible keys in rank order
-  __shared__ double escan[DGD_MAX_CANVAS_LEN];
   __shared__ float hrow[DGD_MAX_CANVAS_LEN];
   __shared__ int ired[kWaves];
   __shared__ double s_mean;
+  __shared__ int s_acc;
   const int tid = threadIdx.x;
   const int L = a.L;
   const size_t rbase = (size_t)c * L;
@@ -1235,32 +1235,37 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
       }
     }
     __syncthreads();
-    // exclusive float64 running sum over the ranks, in rank order
+    // Exclusive float64 running sum over the ranks, in rank order.  Entropies
+    // are >= 0 and rounding is monotone, so the sums never decrease: the
+    // accepted ranks are the prefix before the first sum above the bound,
+    // and the scan stops there.
+    const double bound = (double)a.bound[c];
     if (tid == 0) {
       double run = 0.0;
-      int r0 = 0;
-      for (; r0 + 16 <= n_elig; r0 += 16) {   // 16 ranks per batch: the LDS reads overlap
+      int n_acc = n_elig;
+      for (int r0 = 0; r0 < n_elig && n_acc == n_elig; r0 += 16) {   // 16 ranks per batch: the LDS reads overlap
+        const int nb = min(16, n_elig - r0);
         double h[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) h[j] = (double)__uint_as_float((unsigned)(ranked[r0 + j] >> 32));
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          escan[r0 + j] = run;
+        for (int j = 0; j < 16; ++j)
+          h[j] = j < nb ? (double)__uint_as_float((unsigned)(ranked[r0 + j] >> 32)) : 0.0;
+        for (int j = 0; j < nb; ++j) {
+          if (run > bound) {
+            n_acc = r0 + j;
+            break;
+          }
           run += h[j];
         }
       }
-      for (; r0 < n_elig; ++r0) {
-        escan[r0] = run;
-        run += (double)__uint_as_float((unsigned)(ranked[r0] >> 32));
-      }
+      s_acc = n_acc;
     }
     __syncthreads();
-    const double bound = (double)a.bound[c];
+    const int n_acc = s_acc;
     const uint32_t k0 = a.key[c][0], k1 = a.key[c][1];
     for (int rk = tid; rk < n_elig; rk += kThreads) {
       const int p = (int)(ranked[rk] & 0xffffffffu);
       const size_t idx = cbase + p;
-      if (escan[rk] <= bound) {
+      if (rk < n_acc) {
         a.canvas[idx] = a.rowTok[rbase + p];
         a.committed[idx] = 1;
         if (a.commit_step) a.commit_step[idx] = (int16_t)a.step;
