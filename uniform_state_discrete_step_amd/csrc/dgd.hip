@@ -1136,50 +1136,86 @@ __device__ inline int block_sum_i32(int v, int* red) {
   return out;
 }
 
-// Commit phase of one canvas, run by one workgroup.  The per-position
-// results are read from memory once, into LDS.  The two float64 running sums
-// the rule defines (the mean entropy over positions 0..L-1, and the exclusive
-// prefix over the ranked entropies) are added by one lane in that order, so
-// they are the same doubles however many threads run.
+// Block-wide sums of one double and two ints in a fixed order: each wave
+// adds its lanes by an xor butterfly (every lane pairs the same values, so
+// all lanes hold the same sum), then the wave sums are added in wave order.
+// The double result therefore never depends on timing.
+struct BlockSums {
+  double d;
+  int i0, i1;
+};
+__device__ inline BlockSums block_sums(double d, int i0, int i1, double* dred, int* ired) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    d += __shfl_xor(d, off);
+    i0 += __shfl_xor(i0, off);
+    i1 += __shfl_xor(i1, off);
+  }
+  if (lane == 0) {
+    dred[wave] = d;
+    ired[2 * wave] = i0;
+    ired[2 * wave + 1] = i1;
+  }
+  __syncthreads();
+  BlockSums o{0.0, 0, 0};
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    o.d += dred[w];
+    o.i0 += ired[2 * w];
+    o.i1 += ired[2 * w + 1];
+  }
+  __syncthreads();
+  return o;
+}
+
+typedef unsigned long long u64x2_t __attribute__((ext_vector_type(2)));
+
+// Commit phase of one canvas, run by one workgroup.  Every per-position
+// input is read from memory once, into LDS, before the canvas's done flag is
+// tested, so all of these loads are in flight together.  The mean entropy is
+// a float64 sum in a fixed pairwise order (block_sums); the exclusive prefix
+// over the ranked entropies is added by one lane in rank order.  Both are the
+// same doubles whatever the timing.
 __device__ void commit_canvas(const CommitArgs& a, int c) {
-  __shared__ unsigned long long keys[DGD_MAX_CANVAS_LEN];    // (entropy bits, position)
+  // (entropy bits, position) of each eligible position, ~0 otherwise; two
+  // padding keys (~0) after the last let the ranking read keys in pairs
+  __shared__ __attribute__((aligned(16))) unsigned long long keys[DGD_MAX_CANVAS_LEN + 2];
   __shared__ unsigned long long ranked[DGD_MAX_CANVAS_LEN];  // eligible keys in rank order
-  __shared__ float hrow[DGD_MAX_CANVAS_LEN];
-  __shared__ int ired[kWaves];
-  __shared__ double s_mean;
+  __shared__ int32_t stok[DGD_MAX_CANVAS_LEN];               // sampled token
+  __shared__ int32_t sam[DGD_MAX_CANVAS_LEN];                // argmax
+  __shared__ uint8_t sopen[DGD_MAX_CANVAS_LEN];              // not committed before this step
+  __shared__ double dred[kWaves];
+  __shared__ int ired[2 * kWaves];
   __shared__ int s_acc;
   const int tid = threadIdx.x;
   const int L = a.L;
   const size_t rbase = (size_t)c * L;
   const size_t cbase = (size_t)c * a.G + (size_t)a.block * L;
 
+  double hs = 0.0;   // this thread's positions, in order
   int moved = 0, elig = 0;
   for (int p = tid; p < L; p += kThreads) {
     const float h = a.rowH[rbase + p];
     const int am = a.rowA[rbase + p];
-    hrow[p] = h;
-    moved += (am != a.st_prev[rbase + p]);
-    const bool e = a.freeze == 0 || a.committed[cbase + p] == 0;
+    const int tk = a.rowTok[rbase + p];
+    const int prev = a.st_prev[rbase + p];
+    const bool open = a.committed[cbase + p] == 0;
+    sam[p] = am;
+    stok[p] = tk;
+    sopen[p] = open;
+    moved += (am != prev);
+    const bool e = a.freeze == 0 || open;
     keys[p] = e ? (((unsigned long long)__float_as_uint(h) << 32) | (unsigned)p) : ~0ull;
     elig += e;
+    hs += (double)h;
   }
-  __syncthreads();
-  if (tid == 0) {   // mean entropy over the block, positions in order
-    double hs = 0.0;
-    int p = 0;
-    for (; p + 16 <= L; p += 16) {   // 16 values per batch: the LDS reads overlap
-      float h[16];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) h[j] = hrow[p + j];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) hs += (double)h[j];
-    }
-    for (; p < L; ++p) hs += (double)hrow[p];
-    s_mean = hs / (double)L;
-  }
-  const bool stable = block_sum_i32(moved, ired) == 0;   // (its barriers also publish s_mean)
-  const int n_elig = block_sum_i32(elig, ired);
-  const double mean = s_mean;
+  if (tid < 2) keys[L + tid] = ~0ull;
+  if (a.st_done[c]) return;   // uniform: the whole workgroup leaves before any barrier
+  const BlockSums sums = block_sums(hs, moved, elig, dred, ired);
+  const bool stable = sums.i0 == 0;
+  const int n_elig = sums.i1;
+  const double mean = sums.d / (double)L;
   const int sc = stable ? a.st_stable[c] + 1 : 0;
   const bool converged = mean < (double)a.conf && sc >= a.stab;
   const bool final_step = converged || a.step == a.N - 1;
@@ -1188,9 +1224,9 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
   if (final_step) {
     for (int p = tid; p < L; p += kThreads) {
       const size_t idx = cbase + p;
-      const bool open = a.committed[idx] == 0;
+      const bool open = sopen[p];
       if (a.freeze == 0 || open) {
-        a.canvas[idx] = a.final_emit ? a.rowA[rbase + p] : a.rowTok[rbase + p];
+        a.canvas[idx] = a.final_emit ? sam[p] : stok[p];
         a.committed[idx] = 1;
         if (a.commit_step) a.commit_step[idx] = (int16_t)a.step;
         new_commits += open;
@@ -1211,8 +1247,11 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
         const unsigned long long k = keys[p];
         if (k == ~0ull) continue;
         int rank = 0;
-#pragma unroll 16
-        for (int j = 0; j < L; ++j) rank += keys[j] < k;
+#pragma unroll 8
+        for (int j = 0; j < L; j += 2) {
+          const u64x2_t kk = *reinterpret_cast<const u64x2_t*>(keys + j);
+          rank += (kk.x < k) + (kk.y < k);
+        }
         ranked[rank] = k;
       }
     } else {
@@ -1266,7 +1305,7 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
       const int p = (int)(ranked[rk] & 0xffffffffu);
       const size_t idx = cbase + p;
       if (rk < n_acc) {
-        a.canvas[idx] = a.rowTok[rbase + p];
+        a.canvas[idx] = stok[p];
         a.committed[idx] = 1;
         if (a.commit_step) a.commit_step[idx] = (int16_t)a.step;
         ++new_commits;
@@ -1290,7 +1329,7 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
     a.st_new[c] = new_commits;
   }
   // the argmax canvas of this step becomes the reference of the next one
-  for (int p = tid; p < L; p += kThreads) a.st_prev[rbase + p] = a.rowA[rbase + p];
+  for (int p = tid; p < L; p += kThreads) a.st_prev[rbase + p] = sam[p];
 }
 
 // ---------------------------------------------------------------------------
@@ -1368,15 +1407,25 @@ __global__ void __launch_bounds__(kThreads) k_rmsnorm(const uint16_t* __restrict
 // Grid (ceil(L/4), B); one wave per position merges that position's partial
 // records (fixed order: lanes over the groups, then a butterfly).
 __global__ void __launch_bounds__(kThreads) k_merge(const CommitArgs a) {
+  constexpr int kPerLane = kMaxGroups / 64;   // records per lane (P <= kMaxGroups)
   const int c = blockIdx.y;
-  if (a.st_done[c]) return;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int p = blockIdx.x * kWaves + wave;
   if (p >= a.L) return;
   const size_t r = (size_t)c * a.L + p;
   const Rec* pr = a.part + r * a.P;
+  // Every record load is issued before the first is used and before the done
+  // flag is tested (the records lie in the workspace either way), so the
+  // loads overlap instead of queueing behind one another.
+  Rec part[kPerLane];
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j)
+    part[j] = lane + 64 * j < a.P ? rec_load(pr + lane + 64 * j) : rec_empty();
+  if (a.st_done[c]) return;
   Rec rec = rec_empty();
-  for (int i = lane; i < a.P; i += 64) rec = rec_merge(rec, rec_load(pr + i));
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j)
+    if (lane + 64 * j < a.P) rec = rec_merge(rec, part[j]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     const Rec o = rec_shfl_xor(rec, off);
@@ -1828,9 +1877,7 @@ __global__ void __launch_bounds__(kThreads) k_label(const LabelArgs a) {
 // Grid (B): the commit of every canvas that is not done, one workgroup each
 // (the kernel boundary after k_merge publishes the per-position results).
 __global__ void __launch_bounds__(kThreads) k_commit(const CommitArgs a) {
-  const int c = blockIdx.x;
-  if (a.st_done[c]) return;
-  commit_canvas(a, c);
+  commit_canvas(a, blockIdx.x);
 }
 
 // Grid (ceil(L/256), B).
