@@ -244,6 +244,18 @@ def gumbel_words(seed: int, p_abs: np.ndarray, gstep: int, V: int) -> np.ndarray
     return words[:, :V]
 
 
+def gumbel_at(seed: int, p_abs, gstep: int, v) -> np.ndarray:
+    """The Gumbel noise g of given (row, id) pairs: word v & 3 of
+    Philox(key, (v >> 2, p_abs, gstep, 0)), as in gumbel_words, for arrays
+    p_abs and v of one shape (broadcast)."""
+    k0, k1 = seed_key(seed)
+    p_abs, v = np.broadcast_arrays(np.asarray(p_abs, dtype=np.uint64), np.asarray(v, dtype=np.uint64))
+    w = np.stack(philox4x32_10(v >> np.uint64(2), p_abs, np.uint64(gstep), np.uint64(TAG_GUMBEL),
+                               k0, k1), axis=-1)
+    word = np.take_along_axis(w, (v & np.uint64(3)).astype(np.int64)[..., None], axis=-1)[..., 0]
+    return gumbel_from_word(word)
+
+
 def renoise_token(seed: int, p_abs, gstep: int, V: int) -> np.ndarray:
     k0, k1 = seed_key(seed)
     w = philox4x32_10(np.uint64(0), np.asarray(p_abs, dtype=np.uint64), np.uint64(gstep),

@@ -544,6 +544,100 @@ def test_entropy_is_nonnegative_and_at_most_log_v():
 
 
 # ----------------------------------------------------------------------------
+# the top-two gaps that decide the tie bands (argmax_gap on the tempered
+# logits, gap on the Gumbel-perturbed ones)
+# ----------------------------------------------------------------------------
+def _kat_zero_words(golden_dir):
+    """The published Philox4x32-10 output for counter (0,0,0,0) and key (0,0):
+    the Gumbel words of ids 0..3 at seed 0, position 0, global step 0."""
+    with open(os.path.join(golden_dir, "philox4x32_10_kat.txt")) as f:
+        for line in f:
+            if line.startswith("#") or not line.strip():
+                continue
+            r = [int(t, 16) for t in line.split()]
+            if r[:6] == [0] * 6:
+                return r[6:]
+    raise AssertionError("no all-zero known-answer row")
+
+
+def _gumbel_of_word(w):
+    """g = -ln(-ln u), u the midpoint of cell w >> 9 of 2^23 (scalar floats)."""
+    u = ((w >> 9) + 0.5) * 2.0 ** -23
+    return -math.log(-math.log(u))
+
+
+def test_argmax_gap_closed_forms():
+    """argmax_gap = (largest - second largest) / T of the logits; 0 on an exact tie."""
+    z = np.array([[5.0, 1.0, 3.0, 2.0],
+                  [1.0, 5.0, 3.0, 2.0],
+                  [4.0, 4.0, 1.0, 0.0],
+                  [-1.0, -7.0, -1.5, -30.0],
+                  [0.0, 0.0, 0.0, 0.0],
+                  [2.0, 9.0, 9.0 - 2.0 ** -20, -3.0]])
+    T = 0.5
+    st = O.position_stats(z, T, 0, np.arange(z.shape[0]), 0)
+    expect = np.array([2.0, 2.0, 0.0, 0.5, 0.0, 2.0 ** -20]) / T
+    assert np.array_equal(st["argmax_gap"], expect)
+    assert st["argmax"].tolist() == [0, 1, 0, 0, 0, 1]
+
+
+def test_gumbel_gap_on_separated_logits(golden_dir):
+    """Logits 100 apart cannot be reordered by the noise (|g| < 17), so the
+    sample and its runner-up are fixed: y1 = x_top + g_top, y2 = x_next + g_next,
+    with the four g from the published known-answer words (ids 0..3 at seed 0,
+    position 0, global step 0 use exactly that Philox counter and key)."""
+    g = [_gumbel_of_word(w) for w in _kat_zero_words(golden_dir)]
+    for z, T in (([200.0, 0.0, 300.0, 100.0], 1.0), ([0.0, 300.0, 100.0, 200.0], 0.5),
+                 ([300.0, 200.0, 100.0, 0.0], 2.0)):
+        x = np.array(z) / T
+        top, nxt = int(np.argmax(x)), int(np.argsort(x)[-2])
+        st = O.position_stats(np.array([z]), T, 0, [0], 0)
+        assert st["token"][0] == top
+        assert abs(st["y1"][0] - (x[top] + g[top])) < 1e-9
+        assert abs(st["y2"][0] - (x[nxt] + g[nxt])) < 1e-9
+        assert abs(st["gap"][0] - (x[top] - x[nxt] + g[top] - g[nxt])) < 1e-9
+
+
+def test_gumbel_gap_with_one_dominant_logit(golden_dir):
+    """One logit far ahead: the runner-up is the largest noise among the others."""
+    g = [_gumbel_of_word(w) for w in _kat_zero_words(golden_dir)]
+    for k in range(4):
+        z = np.zeros((1, 4))
+        z[0, k] = 1000.0
+        st = O.position_stats(z, 1.0, 0, [0], 0)
+        rest = max(g[v] for v in range(4) if v != k)
+        assert st["token"][0] == k
+        assert abs(st["gap"][0] - (1000.0 + g[k] - rest)) < 1e-9
+
+
+def test_gumbel_gap_on_two_token_rows(golden_dir):
+    """V = 2: y_v = x_v + g_v with the first two known-answer words; the
+    sample is the larger (id 0 on a tie) and the gap |y_0 - y_1|, across the
+    crossover where the noise decides."""
+    g0, g1 = (_gumbel_of_word(w) for w in _kat_zero_words(golden_dir)[:2])
+    cross = g1 - g0                       # x_0 - x_1 at which y_0 = y_1
+    for delta in (-3.0, -0.5, -1e-3, 1e-3, 0.5, 3.0):
+        a = cross + delta
+        z = np.array([[a, 0.0]])
+        st = O.position_stats(z, 1.0, 0, [0], 0)
+        y0, y1 = a + g0, g1
+        assert st["token"][0] == (0 if y0 >= y1 else 1)
+        assert abs(st["gap"][0] - abs(y0 - y1)) < 1e-9
+        assert abs(st["gap"][0] - abs(delta)) < 1e-9
+
+
+def test_gumbel_at_is_the_noise_of_the_row(golden_dir):
+    """gumbel_at picks the same word as gumbel_words, and the known answers."""
+    g = [_gumbel_of_word(w) for w in _kat_zero_words(golden_dir)]
+    assert np.allclose(O.gumbel_at(0, 0, 0, np.arange(4)), g, rtol=0, atol=1e-12)
+    seed, gstep, V = 0x0123456789ABCDEF, 29, 37
+    p = np.array([[0], [5], [1000]])
+    v = np.arange(V)[None, :]
+    assert np.array_equal(O.gumbel_at(seed, p, gstep, v),
+                          O.gumbel_from_word(O.gumbel_words(seed, p[:, 0], gstep, V)))
+
+
+# ----------------------------------------------------------------------------
 # commit rule
 # ----------------------------------------------------------------------------
 def brute_force_commit(h, eligible, bound):
