@@ -7,15 +7,21 @@ resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma_vocab]
                     [--no-cpu-baseline] [--profile-only] [--lm-head-tail] [--sc-topk K]
+    python bench.py --oracle-timing      # the CPU oracle on every workload, no GPU
 
 ``--lm-head-tail`` adds the model's output norm before the projection and the
 logit softcap (c = 30) after it; ``--sc-topk K`` adds the self-conditioning
 top-K of every position (and its embedding sum) to each step.
 
+The timed steps run through the library's own step loop (dgd_run_steps), so
+no Python runs between steps.  Before them: the measured HBM and MFMA
+ceilings, then one instrumented pass of the whole generation with HIP events
+around every kernel of every step (the projection's average launch for
+``roofline``, and the per-step split), then the W warmup steps.
+
 Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the fused
-projection), timed with HIP events on the library's stream in a separate
-instrumented pass; ``cpu_baseline`` times the CPU oracle on a bounded sample
-of the same workload.
+projection); ``cpu_baseline`` times the CPU oracle on a bounded sample of the
+same workload.
 """
 import argparse
 import json
@@ -88,46 +94,79 @@ def measured_ceilings(dgd, torch, table, dev):
                    "v_mfma_f32_32x32x16_bf16 on operands from the table, one wave per SIMD (best of 5)"}
 
 
-def cpu_baseline(wl, W, Hs, tail=None, sc_topk=0):
-    """Time the oracle (as it stands) on a few full steps of the workload."""
-    from oracle import dgd_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = len(os.sched_getaffinity(0))
-    P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,
-                 stability_threshold=wl.stability_threshold, freeze=wl.freeze,
-                 final_emit=wl.final_emit)
-    steps = 2 if sc_topk else 5
-    t0 = time.perf_counter()
-    for c in range(wl.B):
-        st = O.init_block(O.new_state(wl.G, wl.L), 0, wl.L, wl.V, wl.seeds[c])
-        for s in range(steps):
-            st, info = O.step(st, Hs[0, s, c], W, 0, s, P, wl.seeds[c], wl.bounds[c],
-                              tail=None if tail is None else O.Tail(**tail))
-            if sc_topk:
-                prob, ids, _ = O.sc_topk(info["z"], info["T"], sc_topk)
-                O.sc_embed(prob, ids, W, math.sqrt(wl.d))
-    dt = time.perf_counter() - t0
-    cpu_model = ""
+def cpu_model_name():
     try:
         for line in open("/proc/cpuinfo"):
             if line.startswith("model name"):
-                cpu_model = line.split(":", 1)[1].strip()
-                break
+                return line.split(":", 1)[1].strip()
     except OSError:  # pragma: no cover
         pass
+    return ""
+
+
+def time_oracle(wl, W, Hs, steps, threads, tail=None, sc_topk=0):
+    """Seconds the oracle (as it stands) takes for the first `steps` steps of
+    every canvas of block 0, with its BLAS limited to `threads` threads (the
+    rest of the oracle is single-threaded numpy)."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import dgd_oracle as O
+    P = O.Params(N=wl.N, t_min=wl.t_min, t_max=wl.t_max, confidence=wl.confidence,
+                 stability_threshold=wl.stability_threshold, freeze=wl.freeze,
+                 final_emit=wl.final_emit)
+    W64 = O.bf16_to_f64(W)              # the oracle's own widening, once per table
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        for c in range(wl.B):
+            st = O.init_block(O.new_state(wl.G, wl.L), 0, wl.L, wl.V, wl.seeds[c])
+            for s in range(steps):
+                st, info = O.step(st, Hs[0, s, c], W, 0, s, P, wl.seeds[c], wl.bounds[c],
+                                  W64=W64, tail=None if tail is None else O.Tail(**tail))
+                if sc_topk:
+                    prob, ids, _ = O.sc_topk(info["z"], info["T"], sc_topk)
+                    O.sc_embed(prob, ids, W, math.sqrt(wl.d))
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(wl, W, Hs, tail=None, sc_topk=0):
+    """Time the oracle (as it stands) on a few full steps of the workload,
+    BLAS on every core this process may run on."""
+    cores = len(os.sched_getaffinity(0))
+    steps = 2 if sc_topk else 3
+    dt = time_oracle(wl, W, Hs, steps, cores, tail, sc_topk)
     return {
         "value": steps / dt,
         "unit": "steps/s",
         "cores": int(cores),
-        "cpu_model": cpu_model,
+        "cpu_model": cpu_model_name(),
         "kind": "oracle",
         "sample": f"{steps} denoising step(s) of {wl.name} ({wl.B}x{wl.L} positions x V={wl.V}, "
-                  f"d={wl.d}); oracle float64 numpy, projection via BLAS",
+                  f"d={wl.d}); oracle float64 numpy, projection via BLAS on {cores} threads, "
+                  f"the rest of the step single-threaded",
         "seconds": dt,
     }
+
+
+def oracle_timing_all():
+    """Oracle wall time per step on every workload (BLAS on all cores of the
+    affinity set), and single-threaded on the two small ones.  One JSON line."""
+    from uniform_state_discrete_step_amd.inputs import WORKLOADS, make_workload_arrays
+    cores = len(os.sched_getaffinity(0))
+    plan = [("tiny", 8, True), ("small_vocab", 4, True), ("gemma_vocab", 2, False),
+            ("batched", 1, False), ("multi_block", 2, False)]
+    out = {"kind": "oracle timing", "cores": cores, "cpu_model": cpu_model_name(), "workloads": {}}
+    for name, steps, single in plan:
+        wl = WORKLOADS[name]
+        W, Hs = make_workload_arrays(wl, threads=min(16, cores))
+        rec = {"steps_timed": steps, "canvases": wl.B,
+               "s_per_step": time_oracle(wl, W, Hs, steps, cores) / steps}
+        if single:
+            rec["s_per_step_1thread"] = time_oracle(wl, W, Hs, steps, 1) / steps
+        rec["s_per_run"] = rec["s_per_step"] * wl.N * wl.blocks
+        out["workloads"][name] = rec
+        log(f"[bench] oracle {name}: {rec}")
+        del W, Hs
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -150,6 +189,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed loop (for rocprofv3 runs)")
+    ap.add_argument("--oracle-timing", action="store_true",
+                    help="only time the CPU oracle on every workload (no GPU), print one JSON line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="before the timed loop, run one device-to-device copy of this many MiB "
                          "(a known-size kernel against which HBM byte counters are scaled)")
@@ -158,6 +199,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the denoising step of "
               "this library is a single-GPU path.", file=sys.stderr)
         sys.exit(2)
+    if args.oracle_timing:
+        oracle_timing_all()
+        return
 
     import torch
 
@@ -205,21 +249,32 @@ def main():
     torch.cuda.synchronize()
 
     blocks, N = wl.blocks, wl.N
+    total = blocks * N
+    use_c_loop = sc_out is None
 
     def run_steps(k, start=0):
-        """Enqueue k consecutive denoising steps (block starts included)."""
+        """Enqueue k consecutive denoising steps (block starts included),
+        cycling through the generation."""
+        if use_c_loop:
+            # the library's own loop: no per-step Python
+            i = start % total
+            while k > 0:
+                n = min(k, total - i)
+                dgd.dgd_run_steps(Hd.reshape(-1), Wd, canvas, committed, i, n, params, wl.seeds,
+                                  ctx)
+                k -= n
+                i = 0
+            return
         for i in range(start, start + k):
-            g = i % (blocks * N)
-            b, s = divmod(g, N)
+            b, s = divmod(i % total, N)
             if s == 0:
                 dgd.dgd_init_block(canvas, committed, b, params, wl.seeds, ctx)
             dgd.dgd_step(Hd[b, s].reshape(-1), Wd, canvas, committed, b, s, params, wl.seeds, ctx)
-            if sc_out is not None:
-                # the gather reads whole table rows: the row-major copy serves it
-                # (16 contiguous bytes per row per thread; the packed table would
-                # scatter them over 64-byte lines)
-                dgd.dgd_sc_embed(ctx.sc_prob, ctx.sc_id, wl.B * wl.L, args.sc_topk, W_rows,
-                                 dgd.DGD_VOCAB_ROWS, wl.V, wl.d, math.sqrt(wl.d), sc_out)
+            # the gather reads whole table rows: the row-major copy serves it
+            # (16 contiguous bytes per row per thread; the packed table would
+            # scatter them over 64-byte lines)
+            dgd.dgd_sc_embed(ctx.sc_prob, ctx.sc_id, wl.B * wl.L, args.sc_topk, W_rows,
+                             dgd.DGD_VOCAB_ROWS, wl.V, wl.d, math.sqrt(wl.d), sc_out)
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20
@@ -230,6 +285,20 @@ def main():
         torch.cuda.synchronize()
         log(f"[bench] calibration copy of {args.copy_calibration_mib} MiB done")
         del src, dst
+
+    if not args.profile_only:
+        # measured ceilings, then an instrumented pass (HIP events around every
+        # kernel of every step, on the library's stream) -- both before the
+        # timed loop, so they also bring the GPU to its working clocks
+        ceil = measured_ceilings(dgd, torch, Wd, dev)
+        log(f"[bench] measured ceilings: HBM read {ceil['hbm_read_GBs']:.0f} GB/s, "
+            f"MFMA bf16 {ceil['mfma_bf16_TFLOPs']:.0f} TFLOP/s")
+        ctx.time_k1 = True
+        dgd.dgd_run(Hd.reshape(-1), Wd, canvas, committed, params, wl.seeds, ctx)
+        k1_ms, k1_n = ctx.k1_time()
+        tail_ms = ctx.tail_time()
+        ctx.time_k1 = False
+        torch.cuda.synchronize()
 
     log(f"[bench] warmup {args.warmup} steps")
     run_steps(args.warmup)
@@ -254,12 +323,8 @@ def main():
     if args.profile_only:
         return
 
-    # instrumented pass: HIP events around every fused-projection launch
-    ctx.time_k1 = True
-    dgd.dgd_run(Hd.reshape(-1), Wd, canvas, committed, params, wl.seeds, ctx)
-    k1_ms, k1_n = ctx.k1_time()
-    ctx.time_k1 = False
     k1_avg_s = k1_ms / max(k1_n, 1) * 1e-3
+    tail_avg_s = tail_ms / max(k1_n, 1) * 1e-3
     M = wl.B * wl.L
     table_bytes = (dgd.dgd_q4_vocab_bytes(wl.V, wl.d) if layout == dgd.DGD_VOCAB_Q4
                    else wl.V * wl.d * 2)
@@ -274,9 +339,6 @@ def main():
              "frac": hbm_frac} if bound == "hbm" else
             {"bound": "mfma", "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
              "frac": mfma_frac})
-    ceil = measured_ceilings(dgd, torch, Wd, dev)
-    log(f"[bench] measured ceilings: HBM read {ceil['hbm_read_GBs']:.0f} GB/s, "
-        f"MFMA bf16 {ceil['mfma_bf16_TFLOPs']:.0f} TFLOP/s")
     kname = "k_project" if layout == dgd.DGD_VOCAB_ROWS else "k_project_packed"
     traffic = (measured_traffic(kname)
                if wl.name == "gemma_vocab" and not args.lm_head_tail and not args.sc_topk
@@ -316,6 +378,12 @@ def main():
         "ms_per_step_segments": {"n": n_seg, "median": seg_ms_per_step[n_seg // 2],
                                  "min": seg_ms_per_step[0], "max": seg_ms_per_step[-1]},
         "step_frac_of_hbm_floor": (steps_per_s * alg_bytes) / (HBM_PEAK_GBS * 1e9),
+        "step_split_us": {
+            "how": "HIP events on the library's stream around every kernel of each step of one "
+                   "instrumented dgd_run pass before the timed loop; other = timed ms/step minus both",
+            "projection": k1_avg_s * 1e6,
+            "merge_commit": tail_avg_s * 1e6,
+            "other": ms / args.steps * 1e3 - (k1_avg_s + tail_avg_s) * 1e6},
         "roofline": roof,
     }
     if args.label_read:
@@ -337,7 +405,7 @@ def main():
         out["label_read"] = {"n_labels": n, "positions": M, "us_per_call": us,
                              "table_bytes_read": n * wl.d * 2, "vocab_layout": args.layout}
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on one step")
+        log("[bench] timing the CPU oracle on a few steps")
         W_cpu = W
         if layout == dgd.DGD_VOCAB_Q4:
             # the oracle steps on the bf16 table the 4-bit one stands for

@@ -80,14 +80,19 @@ typedef uint16_t dgd_bf16;
 
 /* Layouts of the vocabulary table W_vocab accepted by dgd_step / dgd_run. */
 #define DGD_VOCAB_ROWS   0  /* [V][d] row-major: the tied embedding table as is          */
-#define DGD_VOCAB_PACKED 1
-#define DGD_VOCAB_Q4     2
+#define DGD_VOCAB_PACKED 1  /* the output of dgd_pack_vocab() (MFMA fragment order)      */
+#define DGD_VOCAB_Q4     2  /* the output of dgd_pack_vocab_q4() (4-bit groups)           */
 
 /* Largest self-conditioning top-K (dgd_ctx.sc_topk, dgd_sc_embed). */
 #define DGD_SC_MAX_TOPK 32
 
 /* Most labels one dgd_label_probs call reads. */
-#define DGD_MAX_LABELS 512  /* the output of dgd_pack_vocab() (MFMA fragment order)      */
+#define DGD_MAX_LABELS 512
+
+/* Per-canvas status word of the state block (see the state layout). */
+#define DGD_STATUS_OK        0
+#define DGD_STATUS_NONFINITE 1  /* some position's logits were NaN or +inf (or all -inf):
+                                   the canvas stopped at that step, untouched        */
 
 /* Sampler knobs (node page "Inputs"; TensorSharp doc "3. Sampler contract").
  * Ranges are checked on every call:
@@ -167,12 +172,16 @@ typedef struct dgd_params {
  *   sc_status  device int32[B*L] or NULL: per position, how many parts of the
  *              vocabulary the selection recomputed exactly (0 almost always),
  *              or -1 if its recomputation budget ran out (the K ids are then
- *              the best found, not certified; ids of -1 mark empty slots)
+ *              the best found, not certified; ids of -1 mark empty slots),
+ *              or -2 for a position with non-finite logits (ids -1, NaN
+ *              probabilities; its canvas stops, see DGD_STATUS_NONFINITE)
  * Positions of canvases that are done are not written.
  * Optional host outputs (timing): when k1_ms is not NULL the call records HIP
  * events around every launch of the fused projection kernel, synchronises
  * before returning, and writes the summed kernel time in ms to *k1_ms and the
- * number of launches timed to *k1_launches (if not NULL).                     */
+ * number of launches timed to *k1_launches (if not NULL); when tail_ms is also
+ * set, *tail_ms receives the summed time from the end of each projection to
+ * the end of its step's last kernel (merge, top-K, commit).                  */
 typedef struct dgd_ctx {
   int32_t B, L, V, d, G;
   const float* entropy_bound;
@@ -188,7 +197,7 @@ typedef struct dgd_ctx {
   int16_t* commit_step;
   double*  k1_ms;
   int32_t* k1_launches;
-  int32_t  vocab_layout;   /* DGD_VOCAB_ROWS or DGD_VOCAB_PACKED: how W_vocab is laid out */
+  int32_t  vocab_layout;   /* DGD_VOCAB_ROWS, DGD_VOCAB_PACKED or DGD_VOCAB_Q4 */
   const dgd_bf16* norm_weight;  /* output-norm weights or NULL */
   float    norm_eps;
   float    softcap;
@@ -197,17 +206,39 @@ typedef struct dgd_ctx {
   float*   sc_prob;
   int32_t* sc_id;
   int32_t* sc_status;
+  double*  tail_ms;             /* see the timing outputs above, or NULL */
 } dgd_ctx;
 
-/* State layout (device, int32/float words, in this order):
+/* State layout (device, int32/float words, in this order; the per-canvas
+ * words carry the pack README's honesty readout, "What works today":
+ * converged, committed fraction, steps used; plus a status and the step's
+ * tie counts):
  *   int32 prev_argmax [B*L]  argmax canvas of the previous step of the block
  *   int32 stable_count[B]    consecutive steps with an unchanged argmax canvas
- *   int32 done        [B]    1 once the canvas has taken its final step
+ *   int32 done        [B]    1 once the canvas has taken its final step (or stopped)
  *   int32 steps_used  [B]    steps taken in the current block
  *   int32 converged   [B]    1 if the block ended by the early-stop rule
  *   int32 n_committed [B]    committed positions of the current block
- *   float mean_entropy[B]    mean entropy of the last step, nats
+ *   float mean_entropy[B]    mean entropy of the last step, nats (NaN if stopped)
  *   int32 new_commits [B]    positions committed by the last step
+ *   int32 status      [B]    DGD_STATUS_OK, or DGD_STATUS_NONFINITE: a position
+ *                            of the last step had no finite distribution (NaN
+ *                            or +inf logits, e.g. a non-finite row of H or an
+ *                            fp32 overflow of the projection).  The canvas then
+ *                            stopped: done = 1, converged = 0, canvas, committed
+ *                            mask and prev_argmax untouched; that step's
+ *                            entropy/gap outputs are NaN and argmax/token -1 at
+ *                            the offending positions.  dgd_init_block clears it.
+ *   Tie counts of the last step (positions where a decision rests on a float
+ *   difference below the comparison bands of the step's arithmetic):
+ *   int32 band_sample [B]    positions whose top-two Gumbel-perturbed logits
+ *                            differ by < 1e-4 nats
+ *   int32 band_commit [B]    ranked positions whose entropy lies within 1e-5
+ *                            nats of the last accepted or the first rejected
+ *                            entropy, or that are one of those two ranks with
+ *                            the running sum before it within 1e-5 of the
+ *                            bound (0 on a final step)
+ *   int32 band_conv   [B]    1 if |mean_entropy - confidence| < 1e-5
  * The step reads and writes it; callers may read it after a stream sync, and
  * may overwrite it to resume from a saved state.                            */
 size_t dgd_state_bytes(int32_t B, int32_t L);
@@ -216,17 +247,21 @@ size_t dgd_state_bytes(int32_t B, int32_t L);
  * and per-position results); 0 if the shape is unsupported. */
 size_t dgd_workspace_bytes(int32_t B, int32_t L, int32_t V, int32_t d);
 
-/* Start block `block` of every canvas: uniform initial tokens (Philox word 0
- * of counter (0, p_abs, block, 2)) over positions [block*L, (block+1)*L),
- * committed = 0 there, and a fresh state for the block.  Earlier and later
- * positions are untouched.
+/* Start block `block` of every canvas (walkthrough, "Lazy Sampling": the
+ * first step samples from all-equal logits, i.e. a uniform canvas; node page,
+ * gen_length row: a longer generation runs more blocks): uniform initial
+ * tokens (Philox word 0 of counter (0, p_abs, block, 2)) over positions
+ * [block*L, (block+1)*L), committed = 0 there, and a fresh state for the
+ * block.  Earlier and later positions are untouched.
  *   canvas     device int32[B*G], committed device uint8[B*G]
  *   seed       host uint64[B] (Philox key: low word, high word)            */
 int dgd_init_block(int32_t* canvas, uint8_t* committed, int32_t block,
                    const dgd_params* params, const uint64_t* seed, const dgd_ctx* ctx);
 
-/* One denoising step (block `block`, step `step` in [0, N)) of every canvas
- * that is not done.  H: device bf16[B*L*d], the final hidden states of the B
+/* One denoising step (walkthrough, "Sampling": apply temperature, compute
+ * entropy, keep a low-entropy prefix and renoise the rest, check for early
+ * stopping; taken eagerly, the forward's hidden states H first) for block
+ * `block`, step `step` in [0, N), of every canvas that is not done.  H: device bf16[B*L*d], the final hidden states of the B
  * canvases for this step (row r = c*L + p).  W_vocab: device, the tied
  * embedding table in the layout ctx->vocab_layout names (bf16[V*d] row-major,
  * or dgd_packed_vocab_bytes(V, d) bytes from dgd_pack_vocab).  H and W_vocab
@@ -237,14 +272,26 @@ int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_
              int32_t block, int32_t step, const dgd_params* params, const uint64_t* seed,
              const dgd_ctx* ctx);
 
-/* Whole generation: for every block b in [0, G/L): dgd_init_block, then up
- * to N steps (steps after a canvas is done leave it untouched; nothing
- * synchronises with the host).  H_steps: device bf16[(G/L)*N*B*L*d], laid
+/* Whole generation (walkthrough, "Denoise, stage, commit, and generate";
+ * node page, gen_length row): for every block b in [0, G/L): dgd_init_block,
+ * then up to N steps (steps after a canvas is done leave it untouched;
+ * nothing synchronises with the host).  H_steps: device bf16[(G/L)*N*B*L*d], laid
  * out [block][step][canvas][position][hidden].  Per-step outputs of ctx, if
  * set, hold the last step taken. */
 int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas,
             uint8_t* committed, const dgd_params* params, const uint64_t* seed,
             const dgd_ctx* ctx);
+
+/* Part of a generation, as dgd_run takes it: the n_steps global steps
+ * g = first_step .. first_step + n_steps - 1 in order, where g = b*N + s is
+ * step s of block b; at every s == 0 the block is first started as by
+ * dgd_init_block.  dgd_run is dgd_run_steps(0, (G/L)*N).  A caller resumes a
+ * generation from a saved state by running its remaining steps.
+ * first_step >= 0, n_steps >= 0, first_step + n_steps <= (G/L)*N; H_steps
+ * as for dgd_run (the whole [G/L][N][B][L][d] array). */
+int dgd_run_steps(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas,
+                  uint8_t* committed, int32_t first_step, int32_t n_steps,
+                  const dgd_params* params, const uint64_t* seed, const dgd_ctx* ctx);
 
 /* The self-conditioning input of the next forward from a step's top-K
  * (walkthrough, "Complete DiffusionGemma model": the decoder adds

@@ -15,19 +15,32 @@ fixes for bf16 inputs with fp32 accumulation):
   entropy is within 1e-5 nats of the last accepted or first rejected
   entropy, or it is one of those two ranks and the running sum before it is
   within 1e-5 of the bound;
-* the early-stop decision equal unless |mean entropy - confidence| < 1e-5 or
-  an argmax band event moved the stability test;
+* the early-stop decision equal unless |mean entropy - confidence| < 1e-5,
+  or the oracle's own rule, given the GPU's argmax canvas (whose every
+  difference is a validated argmax band event), reaches the GPU's decision;
 * re-noised and initial tokens bit-exact (pure integer functions);
 * self-conditioning top-K: the same ids unless an id's oracle tempered logit
   is within 1e-4 of the K-th one (the sample band: both rest on the same fp32
   logits), listed best first up to that band, probabilities within 1e-3
   relative (the entropy bar: an error of e nats in x - lse moves p by e) or
   1e-30 absolute (float32 probabilities flush below its normal range).
+* an excused mismatch must itself be a valid choice: the oracle's tempered
+  logit at the GPU's argmax within 1e-5 of the maximum, the oracle's
+  perturbed logit at the GPU's sample within 1e-4 of the largest;
+* the GPU's gap output (top-two Gumbel gap, nats) within 2e-3 nats of the
+  oracle's (two perturbed values, each held to the 1e-3 nats bar of a
+  per-position float output) plus fp32 rounding at their magnitude;
+* band events at most max(3, 0.5%) of the compared position-steps (the
+  expected rates are ~1e-4 per position-step: the top-two spacing of the
+  perturbed values is exponential with mean ~1 nat, that of the tempered
+  logits ~0.02-0.05 nats on the flattest rows).
 Band events are counted, never hidden.
 """
 from __future__ import annotations
 
 import dataclasses
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -43,13 +56,19 @@ TOL_LOGIT_REL = 2e-2
 BAND_SC = 1e-4
 TOL_SC_PROB_REL = 1e-3
 TOL_SC_PROB_ABS = 1e-30
+TOL_GAP = 2 * TOL_ENTROPY
+BAND_CAP_FRAC = 0.005
+BAND_CAP_MIN = 3
+THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 @dataclasses.dataclass
 class Report:
     steps: int = 0
     positions: int = 0
+    stat_rows: int = 0          # position-steps whose statistics were compared with the oracle's
     max_entropy_err: float = 0.0
+    max_gap_err: float = 0.0
     argmax_band: int = 0
     sample_band: int = 0
     commit_band: int = 0
@@ -61,21 +80,68 @@ class Report:
     sc_rows: int = 0
     sc_band: int = 0
     sc_recomputed: int = 0
+    free_steps: int = 0         # free-running steps before the first divergence
+    divergence: tuple = None    # (block, step, canvas) of the first divergence of a free run
+    resyncs: int = 0
     failures: list = dataclasses.field(default_factory=list)
 
     def fail(self, msg):
         if len(self.failures) < 50:
             self.failures.append(msg)
 
+    @property
+    def band_events(self) -> int:
+        return self.argmax_band + self.sample_band + self.commit_band + self.conv_band
+
+    def check_band_rate(self):
+        """Band events may not exceed max(BAND_CAP_MIN, BAND_CAP_FRAC) of the
+        compared position-steps: a systematic error cannot hide in the bands."""
+        n = max(self.stat_rows, 1)
+        cap = max(BAND_CAP_MIN, BAND_CAP_FRAC * n)
+        if self.band_events > cap:
+            self.fail(f"{self.band_events} band events over {n} compared position-steps "
+                      f"(cap {cap:.1f})")
+
     def summary(self) -> str:
-        return (f"steps={self.steps} positions={self.positions} max|dH|={self.max_entropy_err:.2e} "
+        return (f"steps={self.steps} positions={self.positions} compared={self.stat_rows} "
+                f"max|dH|={self.max_entropy_err:.2e} max|dgap|={self.max_gap_err:.2e} "
                 f"bands: argmax={self.argmax_band} sample={self.sample_band} "
                 f"commit={self.commit_band} convergence={self.conv_band} "
                 f"accepted={self.accepted} renoised={self.renoised}"
+                + (f" free steps={self.free_steps} first divergence={self.divergence} "
+                   f"resyncs={self.resyncs}" if self.free_steps or self.divergence else "")
                 + (f" norm rows={self.norm_rows} (1-step diffs {self.norm_inexact})"
                    if self.norm_rows else "")
                 + (f" sc rows={self.sc_rows} band={self.sc_band} recomputed parts="
                    f"{self.sc_recomputed}" if self.sc_rows else ""))
+
+
+def oracle_stats(z, T, seed, p_abs, gstep, threads=None):
+    """O.position_stats over chunks of rows in threads.  Rows are independent
+    in every quantity it returns, so the result is the same as one call."""
+    threads = THREADS if threads is None else threads
+    rows = z.shape[0]
+    p_abs = np.asarray(p_abs)
+    if threads <= 1 or rows < 2 * threads:
+        return O.position_stats(z, T, seed, p_abs, gstep)
+    chunks = [c for c in np.array_split(np.arange(rows), threads) if c.size]
+    with ThreadPoolExecutor(len(chunks)) as ex:
+        parts = list(ex.map(lambda c: O.position_stats(z[c], T, seed, p_abs[c], gstep), chunks))
+    return {k: np.concatenate([pt[k] for pt in parts]) for k in parts[0]}
+
+
+def oracle_step(state, H_bits, W_bits, block, step_idx, P, seed, bound, W64=None, tail=None):
+    """O.step, with the per-position statistics taken by oracle_stats."""
+    if state.done:
+        return state.copy(), {"skipped": True}
+    L, V = H_bits.shape[0], W_bits.shape[0]
+    T = O.temperature(step_idx, P.N, P.t_min, P.t_max)
+    z = O.logits(H_bits, W_bits, tail, W64=W64)
+    stats = oracle_stats(z, T, seed, block * L + np.arange(L), block * P.N + step_idx)
+    new, info = O.step_from_stats(state, stats, block, step_idx, L, V, P, seed, bound)
+    info["T"] = T
+    info["z"] = z
+    return new, info
 
 
 def q4_device_table(W, V, d, device):
@@ -115,27 +181,60 @@ def commit_band_positions(info, bound) -> set:
     return band
 
 
-def compare_stats(rep: Report, tag: str, st: dict, H_gpu, A_gpu, T_gpu, rows=None):
-    """Entropy / argmax / token agreement for the rows of an oracle stats dict."""
+def compare_stats(rep: Report, tag: str, st: dict, gpu: dict, z, T: float, seed: int, p_abs,
+                  gstep: int, rows=None):
+    """Entropy / argmax / sample / gap agreement for the rows of an oracle
+    stats dict.  gpu: the GPU's "entropy", "argmax", "token" and (optional)
+    "gap" of the same rows; z, T: the oracle's logits of those rows and the
+    temperature; seed, p_abs, gstep: the rows' noise coordinates.  Returns the
+    sets of rows whose argmax / sample differ (every one a validated band
+    event, or a recorded failure)."""
+    H_gpu, A_gpu, T_gpu = gpu["entropy"], gpu["argmax"], gpu["token"]
     H_o, A_o, T_o = st["entropy"], st["argmax"], st["token"]
+    n, V = z.shape
+    p_abs = np.asarray(p_abs).reshape(-1)
+    rep.stat_rows += n
     err = float(np.max(np.abs(H_gpu.astype(np.float64) - H_o.astype(np.float64))))
     rep.max_entropy_err = max(rep.max_entropy_err, err)
     if err > TOL_ENTROPY:
         rep.fail(f"{tag}: entropy error {err:.3e} > {TOL_ENTROPY}")
+
+    def where(i):
+        return i if rows is None else rows[i]
+
     am = np.nonzero(A_gpu != A_o)[0]
     for i in am:
-        if st["argmax_gap"][i] < BAND_ARGMAX:
+        a = int(A_gpu[i])
+        x = z[i] / T
+        ok = st["argmax_gap"][i] < BAND_ARGMAX and 0 <= a < V and x[a] >= x.max() - BAND_ARGMAX
+        if ok:
             rep.argmax_band += 1
         else:
-            rep.fail(f"{tag}: argmax differs at row {i if rows is None else rows[i]} "
-                     f"(gpu {A_gpu[i]}, oracle {A_o[i]}, gap {st['argmax_gap'][i]:.3e})")
+            rep.fail(f"{tag}: argmax differs at row {where(i)} (gpu {a}, oracle {A_o[i]}, "
+                     f"gap {st['argmax_gap'][i]:.3e}"
+                     + (f", oracle x at gpu id {x[a]:.7g} vs max {x.max():.7g})" if 0 <= a < V
+                        else ")"))
     tm = np.nonzero(T_gpu != T_o)[0]
     for i in tm:
-        if st["gap"][i] < BAND_SAMPLE:
+        t = int(T_gpu[i])
+        y = (z[i, t] / T + float(O.gumbel_at(seed, p_abs[i], gstep, t))) if 0 <= t < V else -np.inf
+        if st["gap"][i] < BAND_SAMPLE and y >= st["y1"][i] - BAND_SAMPLE:
             rep.sample_band += 1
         else:
-            rep.fail(f"{tag}: token differs at row {i if rows is None else rows[i]} "
-                     f"(gpu {T_gpu[i]}, oracle {T_o[i]}, gap {st['gap'][i]:.3e})")
+            rep.fail(f"{tag}: token differs at row {where(i)} (gpu {t}, oracle {T_o[i]}, "
+                     f"gap {st['gap'][i]:.3e}, oracle y at gpu id {y:.7g} vs y1 {st['y1'][i]:.7g})")
+    if gpu.get("gap") is not None:
+        g_o = st["gap"]
+        fin = np.isfinite(g_o)
+        if np.any(fin):
+            dg = np.abs(gpu["gap"].astype(np.float64)[fin] - g_o[fin])
+            tol = TOL_GAP + 2.0 ** -20 * (np.abs(st["y1"][fin]) + np.abs(st["y2"][fin]))
+            rep.max_gap_err = max(rep.max_gap_err, float(dg.max()))
+            bad = np.nonzero(dg > tol)[0]
+            if bad.size:
+                i = np.nonzero(fin)[0][bad[0]]
+                rep.fail(f"{tag}: gap differs at row {where(i)} (gpu {gpu['gap'][i]:.7g}, "
+                         f"oracle {g_o[i]:.7g})")
     return set(am.tolist()), set(tm.tolist())
 
 
@@ -185,7 +284,9 @@ def compare_step(rep: Report, tag: str, before: O.CanvasState, after: O.CanvasSt
     rep.steps += 1
     rep.positions += L
     st = info["stats"]
-    am_set, tok_set = compare_stats(rep, tag, st, gpu["entropy"], gpu["argmax"], gpu["token"])
+    gstep = block * params.N + step
+    am_set, tok_set = compare_stats(rep, tag, st, gpu, info["z"], info["T"], seed,
+                                    base + np.arange(L), gstep)
     if not np.array_equal(gpu["prev_argmax"], gpu["argmax"]):
         rep.fail(f"{tag}: state prev_argmax is not this step's argmax")
     # untouched regions
@@ -195,8 +296,15 @@ def compare_step(rep: Report, tag: str, before: O.CanvasState, after: O.CanvasSt
 
     gpu_final = bool(gpu["done"])
     if gpu_final != info["final"]:
-        near = abs(info["mean_H"] - float(np.float32(params.confidence))) < BAND_CONV
-        if near or am_set:
+        conf = float(np.float32(params.confidence))
+        near = abs(info["mean_H"] - conf) < BAND_CONV
+        # the oracle's rule on the GPU's argmax canvas (its differences are
+        # validated argmax band events, or have failed above)
+        stable_g = bool(np.all(gpu["argmax"] == before.prev_argmax))
+        count_g = before.stable_count + 1 if stable_g else 0
+        final_g = ((info["mean_H"] < conf and count_g >= params.stability_threshold)
+                   or step == params.N - 1)
+        if near or (am_set and final_g == gpu_final):
             rep.conv_band += 1
         else:
             rep.fail(f"{tag}: final-step decision differs (gpu {gpu_final}, oracle "
@@ -220,7 +328,6 @@ def compare_step(rep: Report, tag: str, before: O.CanvasState, after: O.CanvasSt
 
     band = commit_band_positions(info, bound)
     p_abs = base + np.arange(L)
-    gstep = block * params.N + step
     renoise = O.renoise_token(seed, p_abs, gstep, V)
     for p in range(L):
         if g_com[p] != o_com[p]:
@@ -334,9 +441,31 @@ class Lockstep:
             rep.fail(f"block {b} step {s_idx}: normalised row {r} element {k} differs by "
                      f"{int(ulp.max())} bf16 steps (gpu {g[r, k]:#06x}, oracle {o[r, k]:#06x})")
 
-    def run(self, blocks=None, steps=None, rep: Report = None, progress=None) -> Report:
+    def gpu_state(self, c) -> O.CanvasState:
+        """The GPU's canvas, mask and state of canvas c, as an oracle state."""
+        wl = self.wl
+        sv = self.ctx.state_views()
+        return O.CanvasState(
+            self.canvas[c * wl.G:(c + 1) * wl.G].cpu().numpy().astype(np.int64),
+            self.committed[c * wl.G:(c + 1) * wl.G].cpu().numpy().copy(),
+            sv["prev_argmax"][c * wl.L:(c + 1) * wl.L].cpu().numpy().astype(np.int64),
+            int(sv["stable_count"][c]), bool(int(sv["done"][c])), int(sv["steps_used"][c]))
+
+    def run(self, blocks=None, steps=None, rep: Report = None, progress=None,
+            free=False) -> Report:
+        """Step both sides and compare every step.
+
+        free=False (lockstep): before every step the GPU receives the
+        oracle's state.  free=True: the GPU runs on its own state; after each
+        step its state must equal the oracle's.  At the first step where they
+        part, both had started from the same state, so that step has already
+        been compared as a lockstep step: it must show a counted band event
+        (else it fails).  The oracle's state is then pushed to the GPU
+        (resync) and the run goes on, so every step is still compared."""
         torch, wl, dgd = self.torch, self.wl, self.dgd
         rep = rep or Report()
+        if free:
+            assert steps is None, "a free run takes every step"
         for b in (range(wl.blocks) if blocks is None else blocks):
             self.states = [O.init_block(s, b, wl.L, wl.V, wl.seeds[c])
                            for c, s in enumerate(self.states)]
@@ -346,8 +475,11 @@ class Lockstep:
             for c, s in enumerate(self.states):
                 if not np.array_equal(can[c * wl.G:(c + 1) * wl.G], s.canvas):
                     rep.fail(f"block {b} canvas {c}: initial tokens differ")
+            synced = free
             for s_idx in (range(wl.N) if steps is None else steps):
-                self.push_state()
+                if not synced:
+                    self.push_state()
+                    synced = free
                 dgd.dgd_step(self.Hd[b, s_idx].reshape(-1), self.Wd, self.canvas, self.committed,
                              b, s_idx, self.params, wl.seeds, self.ctx)
                 torch.cuda.synchronize()
@@ -355,66 +487,48 @@ class Lockstep:
                     self.check_norm(rep, b, s_idx)
                 for c in range(wl.B):
                     before = self.states[c]
-                    after, info = O.step(before, self.Hs[b, s_idx, c], self.W, b, s_idx, self.P,
-                                         wl.seeds[c], wl.bounds[c], W64=self.W64, tail=self.tail)
-                    compare_step(rep, f"block {b} step {s_idx} canvas {c}", before, after, info,
-                                 self.pull(c), wl.L, wl.V, b, s_idx, self.P, wl.seeds[c],
-                                 float(np.float32(wl.bounds[c])))
+                    after, info = oracle_step(before, self.Hs[b, s_idx, c], self.W, b, s_idx,
+                                              self.P, wl.seeds[c], wl.bounds[c], W64=self.W64,
+                                              tail=self.tail)
+                    tag = f"block {b} step {s_idx} canvas {c}"
+                    n_bands = rep.band_events
+                    compare_step(rep, tag, before, after, info, self.pull(c), wl.L, wl.V, b, s_idx,
+                                 self.P, wl.seeds[c], float(np.float32(wl.bounds[c])))
                     if self.sc_topk and not info.get("skipped"):
                         K, sl = self.sc_topk, slice(c * wl.L, (c + 1) * wl.L)
-                        compare_sc(rep, f"block {b} step {s_idx} canvas {c}", info["z"],
-                                   info["T"], K,
+                        compare_sc(rep, tag, info["z"], info["T"], K,
                                    self.ctx.sc_prob.cpu().numpy().reshape(-1, K)[sl],
                                    self.ctx.sc_id.cpu().numpy().reshape(-1, K)[sl],
                                    self.ctx.sc_status.cpu().numpy()[sl])
+                    if free and synced:
+                        g = self.gpu_state(c)
+                        same = (np.array_equal(g.canvas, after.canvas)
+                                and np.array_equal(g.committed, after.committed)
+                                and np.array_equal(g.prev_argmax, after.prev_argmax)
+                                and (g.stable_count, g.done, g.steps_used)
+                                == (after.stable_count, after.done, after.steps_used))
+                        if not same:
+                            # both sides started this step from the same state
+                            if rep.band_events == n_bands:
+                                rep.fail(f"free run: {tag} parts from the oracle without a "
+                                         f"band event")
+                            if rep.divergence is None:
+                                rep.divergence = (b, s_idx, c)
+                            rep.resyncs += 1
+                            synced = False
                     self.states[c] = after
+                if free and rep.divergence is None:
+                    rep.free_steps += 1
                 if progress:
                     progress(b, s_idx, rep)
                 if all(s.done for s in self.states):
                     break
+        rep.check_band_rate()
         return rep
 
 
 def free_running(ls: Lockstep, rep: Report = None):
-    """Both sides run the whole generation on their own state, no state is
-    pushed.  After every step the GPU's canvas, committed mask and done flags
-    must equal the oracle's.  At the first step where they differ, both
-    started from the same state, so that step is compared as a lockstep step:
-    it must show a counted band event and no failure; the runs then part
-    legitimately and the comparison stops.  Returns (rep, first divergence or
-    None)."""
-    torch, wl, dgd = ls.torch, ls.wl, ls.dgd
-    rep = rep or Report()
-    states = [O.new_state(wl.G, wl.L) for _ in range(wl.B)]
-    for b in range(wl.blocks):
-        states = [O.init_block(st, b, wl.L, wl.V, wl.seeds[c]) for c, st in enumerate(states)]
-        dgd.dgd_init_block(ls.canvas, ls.committed, b, ls.params, wl.seeds, ls.ctx)
-        for s_idx in range(wl.N):
-            dgd.dgd_step(ls.Hd[b, s_idx].reshape(-1), ls.Wd, ls.canvas, ls.committed, b, s_idx,
-                         ls.params, wl.seeds, ls.ctx)
-            torch.cuda.synchronize()
-            for c in range(wl.B):
-                before = states[c]
-                after, info = O.step(before, ls.Hs[b, s_idx, c], ls.W, b, s_idx, ls.P,
-                                     wl.seeds[c], wl.bounds[c], W64=ls.W64, tail=ls.tail)
-                g = ls.pull(c)
-                same = (np.array_equal(g["canvas"], after.canvas)
-                        and np.array_equal(g["committed"], after.committed)
-                        and bool(g["done"]) == bool(after.done))
-                if not same:
-                    n_before = rep.argmax_band + rep.sample_band + rep.commit_band + rep.conv_band
-                    compare_step(rep, f"free run: block {b} step {s_idx} canvas {c}", before, after,
-                                 info, g, wl.L, wl.V, b, s_idx, ls.P, wl.seeds[c],
-                                 float(np.float32(wl.bounds[c])))
-                    n_after = rep.argmax_band + rep.sample_band + rep.commit_band + rep.conv_band
-                    if n_after == n_before:
-                        rep.fail(f"free run: block {b} step {s_idx} canvas {c} parts from the oracle "
-                                 f"without a band event")
-                    return rep, (b, s_idx, c)
-                if not info.get("skipped"):
-                    rep.steps += 1
-                    rep.positions += wl.L
-                states[c] = after
-            if all(st.done for st in states):
-                break
-    return rep, None
+    """A whole generation with each side on its own state (see Lockstep.run,
+    free=True).  Returns (rep, first divergence or None)."""
+    rep = ls.run(rep=rep, free=True)
+    return rep, rep.divergence

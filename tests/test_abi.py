@@ -34,8 +34,11 @@ def test_library_exports_every_declared_function(lib):
 
 
 def test_state_and_workspace_sizes(lib):
-    assert dgd.dgd_state_bytes(1, 256) == (256 + 7) * 4
-    assert dgd.dgd_state_bytes(8, 256) == (8 * 256 + 56) * 4
+    # prev_argmax per position, then 11 words per canvas (stable count, done,
+    # steps used, converged, committed, mean entropy, new commits, status and
+    # the three band counters)
+    assert dgd.dgd_state_bytes(1, 256) == (256 + 11) * 4
+    assert dgd.dgd_state_bytes(8, 256) == (8 * 256 + 88) * 4
     assert dgd.dgd_state_bytes(0, 16) == 0
     # 256 positions x 256 vocabulary groups x (32-byte record + 16 x 8-byte
     # self-conditioning candidates) dominate
@@ -134,6 +137,18 @@ def test_invalid_step_block_and_pointers_are_refused(lib):
     assert lib.dgd_step(FAKE, FAKE, FAKE, FAKE, 0, 0, ctypes.byref(p), None, ctypes.byref(_ctx())) == dgd.DGD_EINVAL
     assert lib.dgd_step(FAKE, FAKE, FAKE, FAKE, 0, 0, None, None, ctypes.byref(_ctx())) == dgd.DGD_EINVAL
     assert lib.dgd_run(FAKE, FAKE, FAKE, FAKE, ctypes.byref(p), None, None) == dgd.DGD_EINVAL
+    s1 = (ctypes.c_uint64 * 1)(0)
+    c = _ctx()                                     # G/L = 1 block of N = 8 steps
+    for first, n in ((-1, 1), (0, -1), (0, 9), (8, 1), (5, 4)):
+        assert lib.dgd_run_steps(FAKE, FAKE, FAKE, FAKE, first, n, ctypes.byref(p), s1,
+                                 ctypes.byref(c)) == dgd.DGD_EINVAL, (first, n)
+    assert lib.dgd_run_steps(None, FAKE, FAKE, FAKE, 0, 1, ctypes.byref(p), s1,
+                             ctypes.byref(c)) == dgd.DGD_EINVAL
+    assert lib.dgd_run_steps(FAKE, FAKE, FAKE, FAKE, 0, 1, None, s1,
+                             ctypes.byref(c)) == dgd.DGD_EINVAL
+    # an empty range is a valid call that enqueues nothing
+    assert lib.dgd_run_steps(FAKE, FAKE, FAKE, FAKE, 8, 0, ctypes.byref(p), s1,
+                             ctypes.byref(c)) == dgd.DGD_OK
     s = (ctypes.c_uint64 * 1)(0)
     assert lib.dgd_init_block(FAKE, FAKE, 3, ctypes.byref(p), s, ctypes.byref(_ctx())) == dgd.DGD_EINVAL
     assert lib.dgd_init_block(None, FAKE, 0, ctypes.byref(p), s, ctypes.byref(_ctx())) == dgd.DGD_EINVAL

@@ -2,23 +2,30 @@
 configuration the benchmark times (packed vocabulary table), and on the
 row-major table.
 
-The oracle cannot recompute every position of every step at these sizes, so
-the checks are split:
-* per-position statistics (entropy, argmax, sampled token) of sampled rows
-  at sampled steps, recomputed by the oracle one row at a time;
-* the whole step's decision logic (early stop, sort, entropy bound, sample
-  write, re-noise) at EVERY step: the oracle's step rule is applied to the
-  GPU's own per-position statistics and must reproduce the GPU's new canvas,
-  committed mask and state bit for bit (same inputs, so no tie band);
-* invariants that hold at any size (monotone commits, frozen tokens, range).
-Plus batch invariance (a canvas in the batched run equals the same canvas run
-alone) and run-to-run determinism.
+* The headline workload (256 positions) on the packed table is compared
+  position by position at every step: a free run (the GPU on its own state)
+  with a lockstep comparison of every step, resynchronised from the oracle
+  after a band event (tests/parity.py, Lockstep.run with free=True).  Its
+  logits are checked on one row of every 32-position MFMA block.
+* The other full-size runs compare per-position statistics (entropy,
+  argmax, sample, gap) on one row of every 32-position block of every canvas
+  at sampled steps, recomputed by the oracle for those rows, and the whole
+  step's decision logic (early stop, sort, entropy bound, sample write,
+  re-noise) at EVERY step: the oracle's step rule applied to the GPU's own
+  per-position statistics must reproduce the GPU's new canvas, committed
+  mask and state bit for bit (same inputs, so no tie band).
+* Invariants that hold at any size (entropy range), batch invariance (a
+  canvas in the batched run equals the same canvas run alone) and run-to-run
+  determinism.
+Long tests append progress lines to gpurun_out/test_progress.log.
 """
 import numpy as np
 import pytest
 
 from oracle import dgd_oracle as O
-from tests.parity import Report, compare_sc, compare_stats, q4_device_table
+from tests.parity import (BAND_CONV, BAND_SAMPLE, TOL_LOGIT_REL, Lockstep, Report,
+                          commit_band_positions, compare_sc, compare_stats, oracle_stats,
+                          q4_device_table)
 from uniform_state_discrete_step_amd.inputs import (WORKLOADS, make_workload_arrays, quantize_q4,
                                                     shrink)
 
@@ -31,6 +38,20 @@ def dev():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     return torch.device("cuda:0")
+
+
+def block_rows(L, rng):
+    """One random row in every 32-position block (the MFMA's position blocks)."""
+    return np.array([b0 + int(rng.integers(min(32, L - b0))) for b0 in range(0, L, 32)])
+
+
+def progress(msg):
+    """A progress line for long runs (outside pytest's capture)."""
+    import os
+    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
+    os.makedirs(d, exist_ok=True)
+    with open(os.path.join(d, "test_progress.log"), "a") as f:
+        f.write(msg + "\n")
 
 
 class FullRun:
@@ -83,16 +104,22 @@ class FullRun:
             sv["prev_argmax"][c * wl.L:(c + 1) * wl.L].cpu().numpy().astype(np.int64),
             int(sv["stable_count"][c]), bool(int(sv["done"][c])), int(sv["steps_used"][c]))
 
-    def sampled_rows(self, rep, b, s, rows_per_canvas):
+    def sampled_rows(self, rep, b, s):
+        """Statistics of one row in every 32-position block of every canvas."""
         wl = self.wl
         if self.W64 is None:
             self.W64 = O.bf16_to_f64(self.W)
         T = O.temperature(s, wl.N, wl.t_min, wl.t_max)
         rng = np.random.default_rng([b, s])
+        H = self.ctx.entropy.cpu().numpy()
+        A = self.ctx.argmax.cpu().numpy().astype(np.int64)
+        Tk = self.ctx.token.cpu().numpy().astype(np.int64)
+        gap = self.ctx.gap.cpu().numpy()
         for c in range(wl.B):
-            rows = np.sort(rng.choice(wl.L, size=rows_per_canvas, replace=False))
+            rows = block_rows(wl.L, rng)
             z = O.logits(self.Hs[b, s, c][rows], self.W, self.tail, W64=self.W64)
-            st = O.position_stats(z, T, wl.seeds[c], b * wl.L + rows, b * wl.N + s)
+            p_abs, gstep = b * wl.L + rows, b * wl.N + s
+            st = oracle_stats(z, T, wl.seeds[c], p_abs, gstep)
             sl = slice(c * wl.L, (c + 1) * wl.L)
             if self.sc_topk:
                 K = self.sc_topk
@@ -100,12 +127,30 @@ class FullRun:
                            self.ctx.sc_prob.cpu().numpy().reshape(-1, K)[sl][rows],
                            self.ctx.sc_id.cpu().numpy().reshape(-1, K)[sl][rows],
                            self.ctx.sc_status.cpu().numpy()[sl][rows], rows=rows)
-            compare_stats(rep, f"block {b} step {s} canvas {c} rows {rows.tolist()}", st,
-                          self.ctx.entropy[sl].cpu().numpy()[rows],
-                          self.ctx.argmax[sl].cpu().numpy().astype(np.int64)[rows],
-                          self.ctx.token[sl].cpu().numpy().astype(np.int64)[rows], rows=rows)
+            gpu = {"entropy": H[sl][rows], "argmax": A[sl][rows], "token": Tk[sl][rows],
+                   "gap": gap[sl][rows]}
+            compare_stats(rep, f"block {b} step {s} canvas {c}", st, gpu, z, T, wl.seeds[c],
+                          p_abs, gstep, rows=rows)
 
-    def run(self, sample_every=8, rows_per_canvas=4, blocks=None):
+    def check_band_counters(self, rep, tag, c, info, gap):
+        """The state's tie counts of the step against the same counts taken
+        by the step rule on the GPU's own statistics (equal numbers, so equal
+        counts; the convergence flag may differ only when the float64 mean,
+        summed in another order, lies on the band's edge)."""
+        sv = self.ctx.state_views()
+        if int(sv["status"][c]) != 0:
+            rep.fail(f"{tag}: status {int(sv['status'][c])} on finite inputs")
+        n_sample = int(np.count_nonzero(gap.astype(np.float64) < BAND_SAMPLE))
+        n_commit = len(commit_band_positions(info, float(np.float32(self.wl.bounds[c]))))
+        if (int(sv["band_sample"][c]), int(sv["band_commit"][c])) != (n_sample, n_commit):
+            rep.fail(f"{tag}: band counters (sample, commit) = ({int(sv['band_sample'][c])}, "
+                     f"{int(sv['band_commit'][c])}), expected ({n_sample}, {n_commit})")
+        dconf = abs(info["mean_H"] - float(np.float32(self.wl.confidence)))
+        if int(sv["band_conv"][c]) != int(dconf < BAND_CONV) and abs(dconf - BAND_CONV) > 1e-12:
+            rep.fail(f"{tag}: convergence band flag {int(sv['band_conv'][c])} "
+                     f"(|mean - confidence| = {dconf:.3e})")
+
+    def run(self, sample_every=8, blocks=None):
         torch, wl, dgd = self.torch, self.wl, self.dgd
         rep = Report()
         for b in (range(wl.blocks) if blocks is None else blocks):
@@ -124,6 +169,7 @@ class FullRun:
                 H = self.ctx.entropy.cpu().numpy()
                 A = self.ctx.argmax.cpu().numpy().astype(np.int64)
                 T = self.ctx.token.cpu().numpy().astype(np.int64)
+                gap = self.ctx.gap.cpu().numpy()
                 for c in range(wl.B):
                     sl = slice(c * wl.L, (c + 1) * wl.L)
                     stats = {"entropy": H[sl], "argmax": A[sl], "token": T[sl]}
@@ -140,12 +186,16 @@ class FullRun:
                         rep.fail(f"{tag}: state differs from the step rule")
                     if not np.all((H[sl] >= 0) & (H[sl] <= np.log(wl.V) + 1e-3)):
                         rep.fail(f"{tag}: entropy out of [0, ln V]")
+                    if not info.get("skipped"):
+                        self.check_band_counters(rep, tag, c, info, gap[sl])
                     rep.steps += 1
                     rep.positions += wl.L
                 if s % sample_every == 0 or s == wl.N - 1:
-                    self.sampled_rows(rep, b, s, rows_per_canvas)
+                    self.sampled_rows(rep, b, s)
+                    progress(f"{wl.name} block {b} step {s}: {rep.summary()}")
                 if all(self.gpu_state(c).done for c in range(wl.B)):
                     break
+        rep.check_band_rate()
         return rep
 
 
@@ -154,25 +204,70 @@ def _check(rep, name):
     assert not rep.failures, "\n".join(rep.failures)
 
 
-@pytest.mark.parametrize("layout", [1, 0], ids=["packed", "rows"])
-def test_gemma_vocab_full_run(dev, layout):
+def test_gemma_vocab_every_position_every_step(dev):
+    """The benchmarked configuration (packed table, 256 positions: one
+    256 x 256 tile per workgroup, four tiles per vocabulary group) against
+    the oracle at every position of every step: a free run, each step also
+    compared in lockstep, resynchronised after a band event."""
+    import time
     wl = WORKLOADS["gemma_vocab"]
-    _check(FullRun(wl, dev, layout=layout).run(sample_every=6, rows_per_canvas=6),
-           f"{wl.name} layout={layout}")
+    W, Hs = make_workload_arrays(wl, threads=16)
+    ls = Lockstep(wl, W, Hs, dev, layout=1)
+    t0 = time.perf_counter()
+
+    def prog(b, s, rep):
+        progress(f"{wl.name} free run step {s} ({time.perf_counter() - t0:.0f}s): {rep.summary()}")
+
+    rep = ls.run(free=True, progress=prog)
+    print(f"\n[{wl.name} packed, every position] {rep.summary()}", flush=True)
+    assert not rep.failures, "\n".join(rep.failures)
+    assert rep.steps == wl.N and rep.stat_rows == wl.N * wl.L
+
+
+def test_gemma_vocab_logits_on_sampled_rows(dev):
+    """Full-size logits (packed table) on one row of every 32-position block,
+    at two steps, within the 2e-2 relative bar."""
+    import torch
+    wl = WORKLOADS["gemma_vocab"]
+    W, Hs = make_workload_arrays(wl, threads=16)
+    ls = Lockstep(wl, W, Hs, dev, logits=True, layout=1)
+    W64 = ls.W64
+    worst = 0.0
+    for s in (0, 29):
+        ls.states = [O.init_block(O.new_state(wl.G, wl.L), 0, wl.L, wl.V, wl.seeds[0])]
+        ls.push_state()
+        ls.dgd.dgd_step(ls.Hd[0, s].reshape(-1), ls.Wd, ls.canvas, ls.committed, 0, s, ls.params,
+                        wl.seeds, ls.ctx)
+        torch.cuda.synchronize()
+        rows = block_rows(wl.L, np.random.default_rng([7, s]))
+        zg = ls.ctx.logits.view(wl.L, wl.V)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+        z = O.projection(Hs[0, s, 0][rows], W, W64=W64)
+        scale = np.maximum(np.abs(z), np.sqrt(np.mean(z * z, axis=1, keepdims=True)))
+        rel = np.abs(zg.astype(np.float64) - z) / np.maximum(scale, 1e-30)
+        worst = max(worst, float(rel.max()))
+        print(f"\n[{wl.name} step {s} rows {rows.tolist()}] logits: max rel err {rel.max():.3e}, "
+              f"max abs err {np.abs(zg - z).max():.3e}", flush=True)
+    assert worst <= TOL_LOGIT_REL
+
+
+def test_gemma_vocab_full_run_rows(dev):
+    """The row-major table at the full size."""
+    wl = WORKLOADS["gemma_vocab"]
+    _check(FullRun(wl, dev, layout=0).run(sample_every=6), f"{wl.name} layout=0")
 
 
 def test_batched_full_run_and_batch_invariance(dev):
     import torch
     wl = WORKLOADS["batched"]
     run = FullRun(wl, dev)
-    _check(run.run(sample_every=12, rows_per_canvas=2), wl.name)
+    _check(run.run(sample_every=6), wl.name)
     # canvas 5 of the batch, run alone, must be bitwise identical
     c = 5
     alone = shrink(wl, name="batched_c5", B=1, seeds=(wl.seeds[c],), bounds=(wl.bounds[c],))
     Hs1 = np.ascontiguousarray(run.Hs[:, :, c:c + 1])
     solo = FullRun(alone, dev, W=run.W, Hs=Hs1, Wd=run.Wd)
     solo.W64 = run.W64
-    _check(solo.run(sample_every=1000, rows_per_canvas=1), alone.name)
+    _check(solo.run(sample_every=1000), alone.name)
     torch.cuda.synchronize()
     assert np.array_equal(solo.canvas.cpu().numpy(),
                           run.canvas[c * wl.G:(c + 1) * wl.G].cpu().numpy())
@@ -185,14 +280,14 @@ def test_gemma_vocab_full_run_with_lm_head_tail(dev):
     from uniform_state_discrete_step_amd.inputs import make_norm_weight
     wl = WORKLOADS["gemma_vocab"]
     tail = O.Tail(norm_weight=make_norm_weight(wl.d, wl.cfg_seed), norm_eps=1e-6, softcap=30.0)
-    _check(FullRun(wl, dev, tail=tail).run(sample_every=6, rows_per_canvas=6),
+    _check(FullRun(wl, dev, tail=tail).run(sample_every=6),
            f"{wl.name} with output norm and softcap")
 
 
 def test_gemma_vocab_full_run_q4_table(dev):
     """The 4-bit table stream at the full size."""
     wl = WORKLOADS["gemma_vocab"]
-    _check(FullRun(wl, dev, layout=2).run(sample_every=6, rows_per_canvas=6),
+    _check(FullRun(wl, dev, layout=2).run(sample_every=6),
            f"{wl.name} 4-bit table")
 
 
@@ -202,7 +297,7 @@ def test_gemma_vocab_full_run_with_self_conditioning(dev):
     wl = WORKLOADS["gemma_vocab"]
     tail = O.Tail(norm_weight=make_norm_weight(wl.d, wl.cfg_seed), norm_eps=1e-6, softcap=30.0)
     run = FullRun(wl, dev, tail=tail, sc_topk=32)
-    rep = run.run(sample_every=8, rows_per_canvas=6)
+    rep = run.run(sample_every=8)
     st = run.ctx.sc_status.cpu().numpy()
     print(f"\nrecomputed parts in the last step: {int(st.sum())}, rows budget-exhausted "
           f"{int((st < 0).sum())}", flush=True)
@@ -212,7 +307,7 @@ def test_gemma_vocab_full_run_with_self_conditioning(dev):
 @pytest.mark.parametrize("layout", [1, 0], ids=["packed", "rows"])
 def test_multi_block_full_run(dev, layout):
     wl = WORKLOADS["multi_block"]
-    _check(FullRun(wl, dev, layout=layout).run(sample_every=16, rows_per_canvas=3),
+    _check(FullRun(wl, dev, layout=layout).run(sample_every=8),
            f"{wl.name} layout={layout}")
 
 
@@ -221,7 +316,7 @@ def test_dgd_run_matches_stepping_and_is_deterministic(dev):
     import torch
     wl = WORKLOADS["gemma_vocab"]
     run = FullRun(wl, dev)
-    rep = run.run(sample_every=1000, rows_per_canvas=1)
+    rep = run.run(sample_every=1000)
     _check(rep, wl.name + " stepped")
     outs = []
     # twice with per-step outputs, once without (the benchmark's configuration)

@@ -4,6 +4,7 @@ Lockstep comparisons at sizes the oracle finishes in seconds, spanning
 several vocabulary tiles, several 64-element hidden chunks and ragged tails,
 plus the degenerate cases of the method.  Criteria: see tests/parity.py.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -108,7 +109,8 @@ def test_philox_words_match_the_oracle(dev, keyed):
     ("tiny", dict(B=3, G=32, seeds=(0, 1, 2**63 + 5), bounds=(0.1, 0.0, 1.0))),
     ("tiny", dict(V=1001, d=72, L=37, B=3, G=74, N=5, seeds=(4, 5, 6), bounds=(0.1, 0.3, 0.05))),
     ("small_vocab", {}),
-], ids=["tiny", "tiny_batched", "ragged", "small_vocab"])
+    ("tiny", dict(V=65536, d=128, L=256, G=256, N=6, cfg_seed=23)),
+], ids=["tiny", "tiny_batched", "ragged", "small_vocab", "full_tile"])
 def test_free_running_generation_matches_the_oracle(dev, name, shape):
     """End to end: whole generations on both sides from their own state."""
     from tests.parity import free_running
@@ -144,6 +146,12 @@ def test_tiny_variants(dev, variant, layout):
     dict(V=4096, d=136, L=70, B=2, G=70, N=6),     # rows straddle 32-row blocks of one tile
     dict(V=1024, d=64, L=600, B=1, G=600, N=4),    # canvas over 512: sorting network path
     dict(V=2048, d=128, L=512, B=2, G=512, N=3),   # largest canvas of the counting-rank path
+    # 256 positions: the benchmark's 256 x 256 tile (eight 32-position blocks
+    # per wave), one tile per vocabulary group ...
+    dict(V=65536, d=128, L=256, B=1, G=256, N=4),
+    # ... and two or three tiles per group, a ragged last tile (100 rows) and
+    # a hidden size of three chunks (the two-chunk ring runs one padding chunk)
+    dict(V=131172, d=192, L=256, B=1, G=256, N=3),
 ])
 def test_ragged_shapes(dev, shape, layout):
     B = shape["B"]
@@ -566,3 +574,62 @@ def test_resume_from_saved_state(dev, layout):
     torch.cuda.synchronize()
     assert np.array_equal(can_c.cpu().numpy(), can_a.cpu().numpy())
     assert np.array_equal(com_c.cpu().numpy(), com_a.cpu().numpy())
+
+
+# ----------------------------------------------------------------------------
+# non-finite logits: the canvas stops with a status, untouched
+# ----------------------------------------------------------------------------
+def test_nonfinite_logits_stop_the_canvas(dev, layout):
+    """A NaN in a row of H (canvas 1, step 2) and a row of the largest finite
+    bf16 value, whose fp32 projection overflows (canvas 0, step 4): at that
+    step the canvas keeps its tokens, mask and argmax reference, its status
+    becomes DGD_STATUS_NONFINITE and it is done; the offending position's
+    entropy and gap are NaN and its ids -1; the other canvas goes on as the
+    oracle does (lockstep), and later steps leave the stopped canvas alone."""
+    import torch
+    from tests.parity import Report, compare_step, oracle_step
+    from uniform_state_discrete_step_amd import dgd
+    wl = shrink(WORKLOADS["tiny"], B=2, G=16, seeds=(0, 1), bounds=(0.1, 0.2))
+    W, Hs = make_workload_arrays(wl, threads=1)
+    Hs = Hs.copy()
+    bad = {(2, 1): 5, (4, 0): 9}                     # (step, canvas) -> position
+    Hs[0, 2, 1, 5, 7] = 0x7FC0                        # NaN
+    Hs[0, 4, 0, 9, :] = 0x7F7F                        # 3.39e38 everywhere
+    ls = Lockstep(wl, W, Hs, dev, layout=layout)
+    ls.states = [O.init_block(st, 0, wl.L, wl.V, wl.seeds[c]) for c, st in enumerate(ls.states)]
+    dgd.dgd_init_block(ls.canvas, ls.committed, 0, ls.params, wl.seeds, ls.ctx)
+    rep = Report()
+    stopped = set()
+    for s_idx in range(6):
+        ls.push_state()
+        dgd.dgd_step(ls.Hd[0, s_idx].reshape(-1), ls.Wd, ls.canvas, ls.committed, 0, s_idx,
+                     ls.params, wl.seeds, ls.ctx)
+        torch.cuda.synchronize()
+        sv = ls.ctx.state_views()
+        for c in range(wl.B):
+            before = ls.states[c]
+            g = ls.pull(c)
+            if (s_idx, c) in bad or c in stopped:
+                p = bad.get((s_idx, c))
+                assert np.array_equal(g["canvas"], before.canvas)
+                assert np.array_equal(g["committed"], before.committed)
+                assert np.array_equal(g["prev_argmax"], before.prev_argmax)
+                assert int(sv["status"][c]) == dgd.DGD_STATUS_NONFINITE
+                assert int(sv["done"][c]) == 1 and int(sv["converged"][c]) == 0
+                if p is not None:
+                    assert int(sv["steps_used"][c]) == s_idx + 1
+                    assert np.isnan(g["entropy"][p]) and np.isnan(g["gap"][p])
+                    assert g["argmax"][p] == -1 and g["token"][p] == -1
+                    ls.states[c] = dataclasses.replace(before, done=True, steps_used=s_idx + 1)
+                    stopped.add(c)
+                continue
+            after, info = oracle_step(before, Hs[0, s_idx, c], W, 0, s_idx, ls.P, wl.seeds[c],
+                                      wl.bounds[c], W64=ls.W64)
+            compare_step(rep, f"step {s_idx} canvas {c}", before, after, info, g, wl.L, wl.V, 0,
+                         s_idx, ls.P, wl.seeds[c], float(np.float32(wl.bounds[c])))
+            if not info.get("skipped"):
+                assert int(sv["status"][c]) == dgd.DGD_STATUS_OK
+            ls.states[c] = after
+    print(f"\n[non-finite rows] {rep.summary()} stopped canvases {sorted(stopped)}", flush=True)
+    assert not rep.failures, "\n".join(rep.failures)
+    assert stopped == {0, 1}

@@ -78,6 +78,20 @@ constexpr float kMasked = -2.0e30f;      // logit (bits) of vocabulary ids past 
 constexpr double kMinTemperature = 1e-4;  // keeps tempered fp32 logits finite
 constexpr double kLog2e = 1.442695040888963407359924681001892137;
 
+// Words per canvas in the state block after prev_argmax: stable_count, done,
+// steps_used, converged, n_committed, mean_entropy, new_commits, status and
+// the three band counters.
+constexpr int kStateWordsPerCanvas = 11;
+
+// Per-position flags the merge leaves for the commit kernel.
+constexpr int32_t kRowNonFinite = 1;    // the position's logits were not all finite
+constexpr int32_t kRowNearSample = 2;   // top-two Gumbel gap below the sample band
+
+// Tie bands of the step's float decisions (nats), counted per canvas.
+constexpr double kBandSample = 1e-4;
+constexpr double kBandCommit = 1e-5;
+constexpr double kBandConv = 1e-5;
+
 struct ProjArgs {
   const uint16_t* H;      // [M][d]
   const uint16_t* W;      // [V][d]
@@ -101,6 +115,7 @@ struct CommitArgs {
   float* rowH;
   int32_t* rowA;
   int32_t* rowTok;
+  int32_t* rowF;          // per-position flags (kRowNonFinite, kRowNearSample)
   float* out_entropy;
   int32_t* out_argmax;
   int32_t* out_token;
@@ -116,6 +131,10 @@ struct CommitArgs {
   int32_t* st_ncomm;
   float* st_mean;
   int32_t* st_new;
+  int32_t* st_status;
+  int32_t* st_bsample;
+  int32_t* st_bcommit;
+  int32_t* st_bconv;
   int32_t B, L, G, V, N, block, step, gstep, freeze, final_emit, stab;
   float conf;
   float bound[DGD_MAX_CANVASES];
@@ -133,6 +152,10 @@ struct InitArgs {
   int32_t* st_ncomm;
   float* st_mean;
   int32_t* st_new;
+  int32_t* st_status;
+  int32_t* st_bsample;
+  int32_t* st_bcommit;
+  int32_t* st_bconv;
   int32_t B, L, G, V, block;
   uint32_t key[DGD_MAX_CANVASES][2];
 };
@@ -1136,34 +1159,36 @@ __device__ inline int block_sum_i32(int v, int* red) {
   return out;
 }
 
-// Block-wide sums of one double and two ints in a fixed order: each wave
+// Block-wide sums of one double and four ints in a fixed order: each wave
 // adds its lanes by an xor butterfly (every lane pairs the same values, so
 // all lanes hold the same sum), then the wave sums are added in wave order.
 // The double result therefore never depends on timing.
 struct BlockSums {
   double d;
-  int i0, i1;
+  int i[4];
 };
-__device__ inline BlockSums block_sums(double d, int i0, int i1, double* dred, int* ired) {
+__device__ inline BlockSums block_sums(double d, int i0, int i1, int i2, int i3, double* dred,
+                                       int* ired) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  int v[4] = {i0, i1, i2, i3};
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     d += __shfl_xor(d, off);
-    i0 += __shfl_xor(i0, off);
-    i1 += __shfl_xor(i1, off);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] += __shfl_xor(v[k], off);
   }
   if (lane == 0) {
     dred[wave] = d;
-    ired[2 * wave] = i0;
-    ired[2 * wave + 1] = i1;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) ired[4 * wave + k] = v[k];
   }
   __syncthreads();
-  BlockSums o{0.0, 0, 0};
+  BlockSums o{0.0, {0, 0, 0, 0}};
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     o.d += dred[w];
-    o.i0 += ired[2 * w];
-    o.i1 += ired[2 * w + 1];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o.i[k] += ired[4 * w + k];
   }
   __syncthreads();
   return o;
@@ -1186,25 +1211,29 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
   __shared__ int32_t sam[DGD_MAX_CANVAS_LEN];                // argmax
   __shared__ uint8_t sopen[DGD_MAX_CANVAS_LEN];              // not committed before this step
   __shared__ double dred[kWaves];
-  __shared__ int ired[2 * kWaves];
+  __shared__ int ired[4 * kWaves];
   __shared__ int s_acc;
+  __shared__ double s_edge_sum[2];   // running sums before ranks n_acc - 1 and n_acc
   const int tid = threadIdx.x;
   const int L = a.L;
   const size_t rbase = (size_t)c * L;
   const size_t cbase = (size_t)c * a.G + (size_t)a.block * L;
 
   double hs = 0.0;   // this thread's positions, in order
-  int moved = 0, elig = 0;
+  int moved = 0, elig = 0, bad = 0, near_sample = 0;
   for (int p = tid; p < L; p += kThreads) {
     const float h = a.rowH[rbase + p];
     const int am = a.rowA[rbase + p];
     const int tk = a.rowTok[rbase + p];
+    const int fl = a.rowF[rbase + p];
     const int prev = a.st_prev[rbase + p];
     const bool open = a.committed[cbase + p] == 0;
     sam[p] = am;
     stok[p] = tk;
     sopen[p] = open;
     moved += (am != prev);
+    bad += (fl & kRowNonFinite) != 0;
+    near_sample += (fl & kRowNearSample) != 0;
     const bool e = a.freeze == 0 || open;
     keys[p] = e ? (((unsigned long long)__float_as_uint(h) << 32) | (unsigned)p) : ~0ull;
     elig += e;
@@ -1212,15 +1241,32 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
   }
   if (tid < 2) keys[L + tid] = ~0ull;
   if (a.st_done[c]) return;   // uniform: the whole workgroup leaves before any barrier
-  const BlockSums sums = block_sums(hs, moved, elig, dred, ired);
-  const bool stable = sums.i0 == 0;
-  const int n_elig = sums.i1;
+  const BlockSums sums = block_sums(hs, moved, elig, bad, near_sample, dred, ired);
+  if (sums.i[2] > 0) {
+    // a position without a distribution (non-finite logits): the canvas
+    // stops with an error status; canvas, mask and argmax reference stay as
+    // they were
+    if (tid == 0) {
+      a.st_status[c] = DGD_STATUS_NONFINITE;
+      a.st_done[c] = 1;
+      a.st_conv[c] = 0;
+      a.st_steps[c] = a.step + 1;
+      a.st_mean[c] = __builtin_nanf("");
+      a.st_new[c] = 0;
+      a.st_bsample[c] = sums.i[3];
+      a.st_bcommit[c] = 0;
+      a.st_bconv[c] = 0;
+    }
+    return;
+  }
+  const bool stable = sums.i[0] == 0;
+  const int n_elig = sums.i[1];
   const double mean = sums.d / (double)L;
   const int sc = stable ? a.st_stable[c] + 1 : 0;
   const bool converged = mean < (double)a.conf && sc >= a.stab;
   const bool final_step = converged || a.step == a.N - 1;
 
-  int new_commits = 0;
+  int new_commits = 0, near_commit = 0;
   if (final_step) {
     for (int p = tid; p < L; p += kThreads) {
       const size_t idx = cbase + p;
@@ -1280,7 +1326,7 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
     // and the scan stops there.
     const double bound = (double)a.bound[c];
     if (tid == 0) {
-      double run = 0.0;
+      double run = 0.0, before_last = 0.0;
       int n_acc = n_elig;
       for (int r0 = 0; r0 < n_elig && n_acc == n_elig; r0 += 16) {   // 16 ranks per batch: the LDS reads overlap
         const int nb = min(16, n_elig - r0);
@@ -1293,13 +1339,32 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
             n_acc = r0 + j;
             break;
           }
+          before_last = run;
           run += h[j];
         }
       }
       s_acc = n_acc;
+      s_edge_sum[0] = before_last;   // before rank n_acc - 1 (the last accepted)
+      s_edge_sum[1] = run;           // before rank n_acc (the first rejected, if any)
     }
     __syncthreads();
     const int n_acc = s_acc;
+    // commit band: positions whose entropy is within kBandCommit of the last
+    // accepted or the first rejected one, and those two ranks when the
+    // running sum before them is within kBandCommit of the bound
+    {
+      const int e0 = n_acc - 1, e1 = n_acc;
+      const bool has0 = e0 >= 0 && e0 < n_elig, has1 = e1 < n_elig;
+      const double h0 = has0 ? (double)__uint_as_float((unsigned)(ranked[e0] >> 32)) : 0.0;
+      const double h1 = has1 ? (double)__uint_as_float((unsigned)(ranked[e1] >> 32)) : 0.0;
+      for (int rk = tid; rk < n_elig; rk += kThreads) {
+        const double h = (double)__uint_as_float((unsigned)(ranked[rk] >> 32));
+        bool nb = (has0 && fabs(h - h0) <= kBandCommit) || (has1 && fabs(h - h1) <= kBandCommit);
+        nb |= (rk == e0 && has0 && fabs(s_edge_sum[0] - bound) <= kBandCommit);
+        nb |= (rk == e1 && has1 && fabs(s_edge_sum[1] - bound) <= kBandCommit);
+        near_commit += nb;
+      }
+    }
     const uint32_t k0 = a.key[c][0], k1 = a.key[c][1];
     for (int rk = tid; rk < n_elig; rk += kThreads) {
       const int p = (int)(ranked[rk] & 0xffffffffu);
@@ -1317,6 +1382,7 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
       }
     }
     new_commits = block_sum_i32(new_commits, ired);
+    near_commit = block_sum_i32(near_commit, ired);
     if (tid == 0) {
       a.st_conv[c] = 0;
       a.st_ncomm[c] = (a.freeze ? (L - n_elig) : 0) + new_commits;
@@ -1327,6 +1393,10 @@ __device__ void commit_canvas(const CommitArgs& a, int c) {
     a.st_steps[c] = a.step + 1;
     a.st_mean[c] = (float)mean;
     a.st_new[c] = new_commits;
+    a.st_status[c] = 0;
+    a.st_bsample[c] = sums.i[3];
+    a.st_bcommit[c] = near_commit;
+    a.st_bconv[c] = fabs(mean - (double)a.conf) < kBandConv ? 1 : 0;
   }
   // the argmax canvas of this step becomes the reference of the next one
   for (int p = tid; p < L; p += kThreads) a.st_prev[rbase + p] = sam[p];
@@ -1434,18 +1504,28 @@ __global__ void __launch_bounds__(kThreads) k_merge(const CommitArgs a) {
   }
   if (lane == 0) {
     const double S = (double)rec.S, A = (double)rec.A;
+    // A NaN or +inf logit leaves a non-finite maximum, sum or moment (NaN
+    // never wins a comparison, so it cannot hide in them); logits that are
+    // all -inf leave no argmax.  Such a position has no distribution: it is
+    // flagged, its entropy is NaN and its ids -1, and the commit kernel stops
+    // the canvas instead of ranking or sampling it.
+    const bool finite = isfinite(rec.m) && isfinite(rec.S) && isfinite(rec.A) &&
+                        isfinite(rec.y1) && rec.S > 0.f && rec.am != kNoIndex &&
+                        rec.i1 != kNoIndex;
     double Hn = kLn2 * (log2(S) - A / S);
-    if (!(Hn > 0.0)) Hn = 0.0;
-    const float H = (float)Hn;
-    const float gap = (float)(((double)rec.y1 - (double)rec.y2) * kLn2);
+    if (Hn < 0.0) Hn = 0.0;   // rounding below the exact minimum (0, a one-hot row)
+    const float H = finite ? (float)Hn : __builtin_nanf("");
+    const float gap = finite ? (float)(((double)rec.y1 - (double)rec.y2) * kLn2) : __builtin_nanf("");
+    const int32_t am = finite ? rec.am : -1, tok = finite ? rec.i1 : -1;
     a.rowM[r] = rec.m;
     a.rowS[r] = rec.S;
     a.rowH[r] = H;
-    a.rowA[r] = rec.am;
-    a.rowTok[r] = rec.i1;
+    a.rowA[r] = am;
+    a.rowTok[r] = tok;
+    a.rowF[r] = (finite ? 0 : kRowNonFinite) | ((double)gap < kBandSample ? kRowNearSample : 0);
     if (a.out_entropy) a.out_entropy[r] = H;
-    if (a.out_argmax) a.out_argmax[r] = rec.am;
-    if (a.out_token) a.out_token[r] = rec.i1;
+    if (a.out_argmax) a.out_argmax[r] = am;
+    if (a.out_token) a.out_token[r] = tok;
     if (a.out_gap) a.out_gap[r] = gap;
   }
 }
@@ -1597,6 +1677,19 @@ __global__ void __launch_bounds__(kThreads) k_sc_topk(const ScArgs a) {
   const int row = blockIdx.x;
   if (a.done[row / a.L]) return;
   const int tid = threadIdx.x;
+  {
+    // a position without a distribution (non-finite logits; its canvas
+    // stops in k_commit): no ids, NaN probabilities, status -2
+    const float m = a.rowM[row], S = a.rowS[row];
+    if (!(isfinite(m) && isfinite(S) && S > 0.f)) {
+      if (tid < a.K) {
+        a.out_prob[(size_t)row * a.K + tid] = __builtin_nanf("");
+        a.out_id[(size_t)row * a.K + tid] = -1;
+      }
+      if (tid == 0 && a.out_status) a.out_status[row] = -2;
+      return;
+    }
+  }
   const int n0 = a.P * kScCand;
   {
     // all loads first (independent), then the keys
@@ -1900,6 +1993,10 @@ __global__ void __launch_bounds__(kThreads) k_init_block(const InitArgs a) {
     a.st_ncomm[c] = 0;
     a.st_mean[c] = 0.f;
     a.st_new[c] = 0;
+    a.st_status[c] = 0;
+    a.st_bsample[c] = 0;
+    a.st_bcommit[c] = 0;
+    a.st_bconv[c] = 0;
   }
 }
 
@@ -2005,7 +2102,7 @@ int hip_fail(hipError_t e, const char* what) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t part, rowM, rowS, rowH, rowA, rowTok, cand, total;
+  size_t part, rowM, rowS, rowH, rowA, rowTok, rowF, cand, total;
   int P;
 };
 
@@ -2020,13 +2117,14 @@ WsLayout ws_layout(int B, int L, int V) {
   w.rowH = off;     off = align256(off + M * sizeof(float));
   w.rowA = off;     off = align256(off + M * sizeof(int32_t));
   w.rowTok = off;   off = align256(off + M * sizeof(int32_t));
+  w.rowF = off;     off = align256(off + M * sizeof(int32_t));
   w.cand = off;     off = align256(off + M * (size_t)w.P * kScCand * sizeof(ScEnt));
   w.total = off;
   return w;
 }
 
 struct StateView {
-  int32_t *prev, *stable, *done, *steps, *conv, *ncomm, *newc;
+  int32_t *prev, *stable, *done, *steps, *conv, *ncomm, *newc, *status, *bsample, *bcommit, *bconv;
   float* mean;
 };
 
@@ -2042,6 +2140,10 @@ StateView state_view(void* state, int B, int L) {
   v.ncomm = s + BL + 4 * (size_t)B;
   v.mean = (float*)(s + BL + 5 * (size_t)B);
   v.newc = s + BL + 6 * (size_t)B;
+  v.status = s + BL + 7 * (size_t)B;
+  v.bsample = s + BL + 8 * (size_t)B;
+  v.bcommit = s + BL + 9 * (size_t)B;
+  v.bconv = s + BL + 10 * (size_t)B;
   return v;
 }
 
@@ -2154,6 +2256,8 @@ int launch_init(int32_t* canvas, uint8_t* committed, int block, const uint64_t* 
   const StateView sv = state_view(ctx->state, ctx->B, ctx->L);
   a.st_prev = sv.prev; a.st_stable = sv.stable; a.st_done = sv.done; a.st_steps = sv.steps;
   a.st_conv = sv.conv; a.st_ncomm = sv.ncomm; a.st_mean = sv.mean; a.st_new = sv.newc;
+  a.st_status = sv.status; a.st_bsample = sv.bsample; a.st_bcommit = sv.bcommit;
+  a.st_bconv = sv.bconv;
   a.B = ctx->B; a.L = ctx->L; a.G = ctx->G; a.V = ctx->V; a.block = block;
   fill_keys(a.key, seed, ctx->B);
   const dim3 grid((ctx->L + kThreads - 1) / kThreads, ctx->B);
@@ -2174,19 +2278,23 @@ struct Timer {
     r = hipEventRecord(e, s);
     return r == hipSuccess ? DGD_OK : hip_fail(r, "hipEventRecord");
   }
+  // Events come in threes per step: before the projection, after it, and
+  // after the step's last kernel.
   int finish(const dgd_ctx* ctx) {
     if (!on) return DGD_OK;
-    double total = 0.0;
+    double total = 0.0, tail = 0.0;
     int n = 0;
     int rc = DGD_OK;
     if (!ev.empty()) {
       hipError_t r = hipEventSynchronize(ev.back());
       if (r != hipSuccess) rc = hip_fail(r, "hipEventSynchronize");
-      for (size_t i = 0; rc == DGD_OK && i + 1 < ev.size(); i += 2) {
-        float ms = 0.f;
+      for (size_t i = 0; rc == DGD_OK && i + 2 < ev.size(); i += 3) {
+        float ms = 0.f, ms2 = 0.f;
         r = hipEventElapsedTime(&ms, ev[i], ev[i + 1]);
+        if (r == hipSuccess) r = hipEventElapsedTime(&ms2, ev[i + 1], ev[i + 2]);
         if (r != hipSuccess) { rc = hip_fail(r, "hipEventElapsedTime"); break; }
         total += ms;
+        tail += ms2;
         ++n;
       }
     }
@@ -2195,6 +2303,7 @@ struct Timer {
     if (rc == DGD_OK) {
       *ctx->k1_ms = total;
       if (ctx->k1_launches) *ctx->k1_launches = n;
+      if (ctx->tail_ms) *ctx->tail_ms = tail;
     }
     return rc;
   }
@@ -2331,12 +2440,15 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   ca.rowH = (float*)(ws + wl.rowH);
   ca.rowA = (int32_t*)(ws + wl.rowA);
   ca.rowTok = (int32_t*)(ws + wl.rowTok);
+  ca.rowF = (int32_t*)(ws + wl.rowF);
   ca.out_entropy = ctx->entropy; ca.out_argmax = ctx->argmax;
   ca.out_token = ctx->token; ca.out_gap = ctx->gap;
   ca.commit_step = ctx->commit_step;
   ca.canvas = canvas; ca.committed = committed;
   ca.st_prev = sv.prev; ca.st_stable = sv.stable; ca.st_done = sv.done; ca.st_steps = sv.steps;
   ca.st_conv = sv.conv; ca.st_ncomm = sv.ncomm; ca.st_mean = sv.mean; ca.st_new = sv.newc;
+  ca.st_status = sv.status; ca.st_bsample = sv.bsample; ca.st_bcommit = sv.bcommit;
+  ca.st_bconv = sv.bconv;
   ca.B = B; ca.L = L; ca.G = ctx->G; ca.V = V; ca.N = N;
   ca.block = block; ca.step = step; ca.gstep = gstep;
   ca.freeze = prm->freeze; ca.final_emit = prm->final_emit; ca.stab = prm->stability_threshold;
@@ -2362,7 +2474,8 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   }
   hipLaunchKernelGGL(k_commit, dim3(B), dim3(kThreads), 0, stream, ca);
   e = hipGetLastError();
-  return e == hipSuccess ? DGD_OK : hip_fail(e, "k_commit launch");
+  if (e != hipSuccess) return hip_fail(e, "k_commit launch");
+  return timer.begin(stream);
 }
 
 }  // namespace
@@ -2376,7 +2489,7 @@ const char* dgd_last_error(void) { return g_err.c_str(); }
 
 size_t dgd_state_bytes(int32_t B, int32_t L) {
   if (B < 1 || L < 1) return 0;
-  return ((size_t)B * L + 7 * (size_t)B) * 4;
+  return ((size_t)B * L + kStateWordsPerCanvas * (size_t)B) * 4;
 }
 
 size_t dgd_workspace_bytes(int32_t B, int32_t L, int32_t V, int32_t d) {
@@ -2423,8 +2536,9 @@ int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_
   return rc ? rc : rt;
 }
 
-int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas, uint8_t* committed,
-            const dgd_params* params, const uint64_t* seed, const dgd_ctx* ctx) {
+int dgd_run_steps(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas,
+                  uint8_t* committed, int32_t first_step, int32_t n_steps,
+                  const dgd_params* params, const uint64_t* seed, const dgd_ctx* ctx) {
   g_err.clear();
   int rc = check_shape(ctx);
   if (rc) return rc;
@@ -2437,19 +2551,38 @@ int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas, u
     return fail(DGD_EINVAL, "H_steps/W_vocab is not 16-byte aligned");
   const int N = params->num_inference_steps;
   const int blocks = ctx->G / ctx->L;
+  const int64_t total = (int64_t)blocks * N;
+  if (first_step < 0 || n_steps < 0 || (int64_t)first_step + n_steps > total)
+    return fail(DGD_EINVAL, "steps [%d, %d + %d) outside the run's %lld steps", first_step,
+                first_step, n_steps, (long long)total);
   const size_t step_elems = (size_t)ctx->B * ctx->L * ctx->d;
   if ((rc = check_tail(ctx, H_steps, (size_t)blocks * N * step_elems * 2))) return rc;
   if ((rc = check_sc(ctx))) return rc;
   Timer timer;
   timer.on = ctx->k1_ms != nullptr;
-  for (int b = 0; b < blocks && rc == DGD_OK; ++b) {
-    rc = launch_init(canvas, committed, b, seed, ctx);
-    for (int s = 0; s < N && rc == DGD_OK; ++s)
-      rc = launch_step(H_steps + ((size_t)b * N + s) * step_elems, W_vocab, canvas, committed, b, s,
-                       params, seed, ctx, timer);
+  for (int g = first_step; g < first_step + n_steps && rc == DGD_OK; ++g) {
+    const int b = g / N, s = g % N;
+    if (s == 0) rc = launch_init(canvas, committed, b, seed, ctx);
+    if (rc == DGD_OK)
+      rc = launch_step(H_steps + (size_t)g * step_elems, W_vocab, canvas, committed, b, s, params,
+                       seed, ctx, timer);
   }
   const int rt = timer.finish(ctx);
   return rc ? rc : rt;
+}
+
+int dgd_run(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas, uint8_t* committed,
+            const dgd_params* params, const uint64_t* seed, const dgd_ctx* ctx) {
+  if (!ctx || !params) {
+    g_err.clear();
+    return fail(DGD_EINVAL, "ctx/params is NULL");
+  }
+  const int64_t total = ctx->L > 0 ? (int64_t)(ctx->G / ctx->L) * params->num_inference_steps : 0;
+  if (total > INT32_MAX) {
+    g_err.clear();
+    return fail(DGD_EINVAL, "too many steps");
+  }
+  return dgd_run_steps(H_steps, W_vocab, canvas, committed, 0, (int32_t)total, params, seed, ctx);
 }
 
 size_t dgd_packed_vocab_bytes(int32_t V, int32_t d) {

@@ -26,8 +26,11 @@ DGD_MAX_CANVAS_LEN = 4096
 DGD_VOCAB_ROWS = 0
 DGD_VOCAB_PACKED = 1
 DGD_VOCAB_Q4 = 2
+DGD_STATUS_OK = 0
+DGD_STATUS_NONFINITE = 1
 
 EXPORTED = ("dgd_state_bytes", "dgd_workspace_bytes", "dgd_init_block", "dgd_step", "dgd_run",
+            "dgd_run_steps",
             "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_q4_vocab_bytes", "dgd_pack_vocab_q4",
             "dgd_sc_embed", "dgd_label_probs",
             "dgd_ceiling_hbm_read", "dgd_ceiling_mfma_bf16", "dgd_debug_philox",
@@ -79,6 +82,7 @@ class DgdCtx(ctypes.Structure):
         ("sc_prob", ctypes.c_void_p),
         ("sc_id", ctypes.c_void_p),
         ("sc_status", ctypes.c_void_p),
+        ("tail_ms", ctypes.POINTER(ctypes.c_double)),
     ]
 
 
@@ -110,6 +114,9 @@ def load_library(path: str = LIB_PATH):
     lib.dgd_run.restype = ctypes.c_int
     lib.dgd_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                             pp, pseed, pc]
+    lib.dgd_run_steps.restype = ctypes.c_int
+    lib.dgd_run_steps.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, pp, pseed, pc]
     lib.dgd_packed_vocab_bytes.restype = ctypes.c_size_t
     lib.dgd_packed_vocab_bytes.argtypes = [ctypes.c_int32, ctypes.c_int32]
     lib.dgd_pack_vocab.restype = ctypes.c_int
@@ -220,6 +227,7 @@ class Context:
                             if commit_trace else None)
         self._k1_ms = ctypes.c_double(0.0)
         self._k1_n = ctypes.c_int32(0)
+        self._tail_ms = ctypes.c_double(0.0)
         self.time_k1 = False
         self.vocab_layout = int(vocab_layout)
         self.norm_weight = norm_weight
@@ -246,11 +254,19 @@ class Context:
             "n_committed": s[BL + 4 * B:BL + 5 * B],
             "mean_entropy": s[BL + 5 * B:BL + 6 * B].view(__import__("torch").float32),
             "new_commits": s[BL + 6 * B:BL + 7 * B],
+            "status": s[BL + 7 * B:BL + 8 * B],
+            "band_sample": s[BL + 8 * B:BL + 9 * B],
+            "band_commit": s[BL + 9 * B:BL + 10 * B],
+            "band_conv": s[BL + 10 * B:BL + 11 * B],
         }
 
     def k1_time(self):
         """(summed projection-kernel ms, launches) of the last timed call."""
         return self._k1_ms.value, self._k1_n.value
+
+    def tail_time(self):
+        """Summed ms from each projection's end to its step's end, last timed call."""
+        return self._tail_ms.value
 
     def as_ctypes(self, stream=None) -> DgdCtx:
         c = DgdCtx()
@@ -278,6 +294,7 @@ class Context:
         if self.time_k1:
             c.k1_ms = ctypes.pointer(self._k1_ms)
             c.k1_launches = ctypes.pointer(self._k1_n)
+            c.tail_ms = ctypes.pointer(self._tail_ms)
         return c
 
 
@@ -317,6 +334,14 @@ def dgd_run(H_steps, W_vocab, canvas, committed, params: DgdParams, seeds, ctx: 
     _check(load_library().dgd_run(_ptr(H_steps, 2), _ptr(W_vocab), _ptr(canvas, 4),
                                   _ptr(committed, 1), ctypes.byref(params), _seeds(seeds),
                                   ctypes.byref(c)))
+
+
+def dgd_run_steps(H_steps, W_vocab, canvas, committed, first_step: int, n_steps: int,
+                  params: DgdParams, seeds, ctx: Context, stream=None):
+    c = ctx.as_ctypes(stream)
+    _check(load_library().dgd_run_steps(_ptr(H_steps, 2), _ptr(W_vocab), _ptr(canvas, 4),
+                                        _ptr(committed, 1), int(first_step), int(n_steps),
+                                        ctypes.byref(params), _seeds(seeds), ctypes.byref(c)))
 
 
 def dgd_packed_vocab_bytes(V: int, d: int) -> int:
