@@ -272,6 +272,26 @@ int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_
              int32_t block, int32_t step, const dgd_params* params, const uint64_t* seed,
              const dgd_ctx* ctx);
 
+/* dgd_step for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same step, with
+ * the same kernels and results, whose scratch is a 32 MiB device array of the
+ * library (one per GPU, held until the process ends) instead of
+ * ctx->workspace, which is ignored (may be NULL).  The call allocates
+ * nothing: no hipMalloc or hipFree, no events (ctx->k1_ms must be NULL).  The
+ * first call on a device looks the array's address up on that device.
+ * Shapes whose scratch exceeds the array are refused with DGD_EUNSUPPORTED:
+ * the step needs 32 B per (position, vocabulary group) record (groups =
+ * min(ceil(V/256), 256)), 24 B per position, and with a top-K 128 B more per
+ * record; e.g. 256 positions at V = 262144 need 2.1 MB (10.5 MB with a
+ * top-K), 2048 positions 16.8 MB (without).  Nothing is carried in the array
+ * from one call to the next, but every call on a GPU uses that GPU's one
+ * array: calls that overlap on one GPU (other streams, other threads) race
+ * and must not be issued.  Everything else (state, outputs, errors) is as
+ * for dgd_step. */
+int dgd_step_noalloc(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas,
+                     uint8_t* committed, int32_t block, int32_t step, const dgd_params* params,
+                     const uint64_t* seed, const dgd_ctx* ctx);
+
 /* Whole generation (walkthrough, "Denoise, stage, commit, and generate";
  * node page, gen_length row): for every block b in [0, G/L): dgd_init_block,
  * then up to N steps (steps after a canvas is done leave it untouched;

@@ -308,3 +308,33 @@ def test_packed_vocab_size_and_refusals(lib):
     # destination overlapping the source
     assert lib.dgd_pack_vocab(FAKE, FAKE + 64 * 64, 64, 64, None) == dgd.DGD_EINVAL
     assert dgd.dgd_last_error()
+
+
+def test_no_alloc_step_refusals(lib):
+    """Refusals of the no-allocation step happen on the host, before any HIP
+    call: invalid arguments as for dgd_step, a shape whose scratch exceeds the
+    library's array, and a timing request (events would be created)."""
+    p = dgd.make_params(N=8)
+    s = (ctypes.c_uint64 * 8)(*range(8))
+
+    def call(ctx, H=FAKE, step=0):
+        return lib.dgd_step_noalloc(H, FAKE, FAKE, FAKE, 0, step, ctypes.byref(p), s,
+                                    ctypes.byref(ctx))
+
+    c = _ctx(workspace=None, workspace_bytes=0)
+    assert call(c, H=None) == dgd.DGD_EINVAL
+    assert call(c, step=8) == dgd.DGD_EINVAL
+    assert call(c, H=FAKE + 8) == dgd.DGD_EINVAL
+    # 8 x 2048 positions x 256 vocabulary groups x 32 B of records = 128 MiB > 32 MiB
+    big = _ctx(B=8, L=2048, G=2048, V=262144, d=2816, workspace=None, workspace_bytes=0)
+    assert call(big) == dgd.DGD_EUNSUPPORTED
+    assert "scratch" in dgd.dgd_last_error()
+    # 2048 positions fit without a top-K, not with one (candidates: 128 B per record)
+    sc = _ctx(B=8, L=256, G=256, V=262144, d=2816, workspace=None, workspace_bytes=0,
+              sc_topk=32, sc_prob=FAKE * 32, sc_id=FAKE * 64, vocab_layout=1)
+    assert call(sc) == dgd.DGD_EUNSUPPORTED
+    t = _ctx(workspace=None, workspace_bytes=0)
+    ms = ctypes.c_double(0.0)
+    t.k1_ms = ctypes.pointer(ms)
+    assert call(t) == dgd.DGD_EINVAL
+    assert "k1_ms" in dgd.dgd_last_error()

@@ -35,6 +35,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <type_traits>
 #include <vector>
@@ -2232,12 +2233,75 @@ int check_knobs(const dgd_ctx* ctx, const uint64_t* seed, bool need_bounds) {
   return DGD_OK;
 }
 
+// Checks shared by the step entry points (own_workspace: the caller's
+// ctx->workspace must be there and large enough).
+int check_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_t* committed,
+               int32_t block, int32_t step, const dgd_params* params, const uint64_t* seed,
+               const dgd_ctx* ctx, bool own_workspace);
+
 int check_workspace(const dgd_ctx* ctx) {
   const WsLayout w = ws_layout(ctx->B, ctx->L, ctx->V);
   if (!ctx->workspace) return fail(DGD_EINVAL, "ctx->workspace is NULL");
   if (((uintptr_t)ctx->workspace & 255) != 0) return fail(DGD_EINVAL, "workspace is not 256-byte aligned");
   if (ctx->workspace_bytes < w.total)
     return fail(DGD_EWORKSPACE, "workspace has %zu bytes, needs %zu", ctx->workspace_bytes, w.total);
+  return DGD_OK;
+}
+
+int check_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_t* committed,
+               int32_t block, int32_t step, const dgd_params* params, const uint64_t* seed,
+               const dgd_ctx* ctx, bool own_workspace) {
+  int rc = check_shape(ctx);
+  if (rc) return rc;
+  if ((rc = check_params(params))) return rc;
+  if ((rc = check_knobs(ctx, seed, true))) return rc;
+  if (own_workspace && (rc = check_workspace(ctx))) return rc;
+  if (!H || !W_vocab || !canvas || !committed) return fail(DGD_EINVAL, "H/W_vocab/canvas/committed is NULL");
+  if (!aligned16(H) || !aligned16(W_vocab)) return fail(DGD_EINVAL, "H/W_vocab is not 16-byte aligned");
+  if ((rc = check_tail(ctx, H, (size_t)ctx->B * ctx->L * ctx->d * 2))) return rc;
+  if ((rc = check_sc(ctx))) return rc;
+  if (block < 0 || block >= ctx->G / ctx->L)
+    return fail(DGD_EINVAL, "block=%d outside [0, %d)", block, ctx->G / ctx->L);
+  if (step < 0 || step >= params->num_inference_steps)
+    return fail(DGD_EINVAL, "step=%d outside [0, %d)", step, params->num_inference_steps);
+  return DGD_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation step
+// ---------------------------------------------------------------------------
+// A workspace per GPU in a file-scope device array, for callers that cannot
+// allocate (code under graph capture, tight serving loops, harnesses that
+// forbid hipMalloc).  Every GPU the library runs on holds its own copy until
+// the process ends.  The array's name in host code is a host-side stand-in,
+// not a device address: its address on a device comes from
+// hipGetSymbolAddress, taken once per device with that device current, and
+// only that pointer reaches kernels.  The step carries no data in it from one
+// call to the next (every byte a step reads, the same step wrote first), so
+// nothing needs clearing; calls that overlap on one GPU race on it.
+constexpr size_t kScratchBytes = 32u << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];   // device address of `scratch` per device, or null
+
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(DGD_EUNSUPPORTED, "device %d: the no-allocation step serves devices 0..%d", dev,
+                kMaxDevices - 1);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255) != 0) return fail(DGD_EHIP, "scratch address %p is unusable", p);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return DGD_OK;
 }
 
@@ -2516,24 +2580,36 @@ int dgd_step(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas, uint8_
              int32_t block, int32_t step, const dgd_params* params, const uint64_t* seed,
              const dgd_ctx* ctx) {
   g_err.clear();
-  int rc = check_shape(ctx);
+  int rc = check_step(H, W_vocab, canvas, committed, block, step, params, seed, ctx, true);
   if (rc) return rc;
-  if ((rc = check_params(params))) return rc;
-  if ((rc = check_knobs(ctx, seed, true))) return rc;
-  if ((rc = check_workspace(ctx))) return rc;
-  if (!H || !W_vocab || !canvas || !committed) return fail(DGD_EINVAL, "H/W_vocab/canvas/committed is NULL");
-  if (!aligned16(H) || !aligned16(W_vocab)) return fail(DGD_EINVAL, "H/W_vocab is not 16-byte aligned");
-  if ((rc = check_tail(ctx, H, (size_t)ctx->B * ctx->L * ctx->d * 2))) return rc;
-  if ((rc = check_sc(ctx))) return rc;
-  if (block < 0 || block >= ctx->G / ctx->L)
-    return fail(DGD_EINVAL, "block=%d outside [0, %d)", block, ctx->G / ctx->L);
-  if (step < 0 || step >= params->num_inference_steps)
-    return fail(DGD_EINVAL, "step=%d outside [0, %d)", step, params->num_inference_steps);
   Timer timer;
   timer.on = ctx->k1_ms != nullptr;
   rc = launch_step(H, W_vocab, canvas, committed, block, step, params, seed, ctx, timer);
   const int rt = timer.finish(ctx);
   return rc ? rc : rt;
+}
+
+int dgd_step_noalloc(const dgd_bf16* H, const dgd_bf16* W_vocab, int32_t* canvas,
+                     uint8_t* committed, int32_t block, int32_t step, const dgd_params* params,
+                     const uint64_t* seed, const dgd_ctx* ctx) {
+  g_err.clear();
+  int rc = check_step(H, W_vocab, canvas, committed, block, step, params, seed, ctx, false);
+  if (rc) return rc;
+  if (ctx->k1_ms)
+    return fail(DGD_EINVAL, "kernel timing (k1_ms) creates HIP events: not offered by the "
+                            "no-allocation step");
+  const WsLayout w = ws_layout(ctx->B, ctx->L, ctx->V);
+  const size_t need = ctx->sc_topk > 0 ? w.total : w.cand;   // candidates only with a top-K
+  if (need > kScratchBytes)
+    return fail(DGD_EUNSUPPORTED, "this shape needs %zu bytes of scratch; the no-allocation step "
+                                  "has %zu", need, kScratchBytes);
+  void* ws = nullptr;
+  if ((rc = scratch_of_current_device(&ws))) return rc;
+  dgd_ctx c = *ctx;
+  c.workspace = ws;
+  c.workspace_bytes = kScratchBytes;
+  Timer timer;   // off: no events
+  return launch_step(H, W_vocab, canvas, committed, block, step, params, seed, &c, timer);
 }
 
 int dgd_run_steps(const dgd_bf16* H_steps, const dgd_bf16* W_vocab, int32_t* canvas,

@@ -30,7 +30,7 @@ DGD_STATUS_OK = 0
 DGD_STATUS_NONFINITE = 1
 
 EXPORTED = ("dgd_state_bytes", "dgd_workspace_bytes", "dgd_init_block", "dgd_step", "dgd_run",
-            "dgd_run_steps",
+            "dgd_run_steps", "dgd_step_noalloc",
             "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_q4_vocab_bytes", "dgd_pack_vocab_q4",
             "dgd_sc_embed", "dgd_label_probs",
             "dgd_ceiling_hbm_read", "dgd_ceiling_mfma_bf16", "dgd_debug_philox",
@@ -111,6 +111,9 @@ def load_library(path: str = LIB_PATH):
     lib.dgd_step.restype = ctypes.c_int
     lib.dgd_step.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                              ctypes.c_int32, ctypes.c_int32, pp, pseed, pc]
+    lib.dgd_step_noalloc.restype = ctypes.c_int
+    lib.dgd_step_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, pp, pseed, pc]
     lib.dgd_run.restype = ctypes.c_int
     lib.dgd_run.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                             pp, pseed, pc]
@@ -326,6 +329,15 @@ def dgd_step(H, W_vocab, canvas, committed, block, step, params: DgdParams, seed
     _check(load_library().dgd_step(_ptr(H, 2), _ptr(W_vocab), _ptr(canvas, 4),
                                    _ptr(committed, 1), int(block), int(step),
                                    ctypes.byref(params), _seeds(seeds), ctypes.byref(c)))
+
+
+def dgd_step_noalloc(H, W_vocab, canvas, committed, block, step, params: DgdParams, seeds,
+                     ctx: Context, stream=None):
+    """dgd_step with the library's own per-GPU scratch instead of ctx's workspace."""
+    c = ctx.as_ctypes(stream)
+    _check(load_library().dgd_step_noalloc(_ptr(H, 2), _ptr(W_vocab), _ptr(canvas, 4),
+                                           _ptr(committed, 1), int(block), int(step),
+                                           ctypes.byref(params), _seeds(seeds), ctypes.byref(c)))
 
 
 def dgd_run(H_steps, W_vocab, canvas, committed, params: DgdParams, seeds, ctx: Context,
