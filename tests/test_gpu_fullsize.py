@@ -17,7 +17,7 @@ row-major table.
 * Invariants that hold at any size (entropy range), batch invariance (a
   canvas in the batched run equals the same canvas run alone) and run-to-run
   determinism.
-Long tests append progress lines to gpurun_out/test_progress.log.
+Long tests append progress lines to the file DGD_PROGRESS_LOG names, if set.
 """
 import numpy as np
 import pytest
@@ -46,12 +46,14 @@ def block_rows(L, rng):
 
 
 def progress(msg):
-    """A progress line for long runs (outside pytest's capture)."""
+    """A progress line for long runs, appended to the file DGD_PROGRESS_LOG
+    names (outside pytest's capture), if it is set."""
     import os
-    d = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "gpurun_out")
-    os.makedirs(d, exist_ok=True)
-    with open(os.path.join(d, "test_progress.log"), "a") as f:
-        f.write(msg + "\n")
+    path = os.environ.get("DGD_PROGRESS_LOG")
+    if path:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path, "a") as f:
+            f.write(msg + "\n")
 
 
 class FullRun:
