@@ -415,6 +415,24 @@ int dgd_ceiling_hbm_read(const void* buf, size_t bytes, uint32_t* sink, void* st
 int dgd_ceiling_mfma_bf16(const void* ops, size_t bytes, int64_t rounds, int32_t workgroups, float* sink,
                           void* stream);
 
+/* Measurement helper (not part of the step): phase times of the packed
+ * projection, for a profile of where its time goes.  Only a library built
+ * with DGD_PHASE_TIMING defined records them (build.py writes that build as
+ * libdgd_phase.so beside libdgd.so); its packed projection then stores, for
+ * workgroups 0..1023 and each of their 4 waves, 16 slots of 64 bits:
+ *   slot 0        100 MHz wall clock at kernel start; slot 1 shader clock there
+ *   slot 2+3t     wall clock at the start of tile t (t = 0..3, the first four
+ *                 vocabulary tiles of the workgroup)
+ *   slot 3+3t     wall clock at the end of tile t's K loop (all MFMAs issued)
+ *   slot 4+3t     wall clock at the end of tile t's epilogue
+ *   slot 14       wall clock at kernel end; slot 15 shader clock there
+ * at entry (workgroup*4 + wave)*16 + slot.  Each launch overwrites the last;
+ * slots of tiles a workgroup does not run keep older values.
+ *   dst  host uint64[n], n <= 1024*4*16; copied synchronously, so the caller
+ *        synchronises its stream first.
+ * Returns DGD_EUNSUPPORTED (nothing copied) in a library built without it. */
+int dgd_phase_times(uint64_t* dst, size_t n);
+
 /* Description of the last failure on the calling thread ("" if none). */
 const char* dgd_last_error(void);
 

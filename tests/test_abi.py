@@ -338,3 +338,21 @@ def test_no_alloc_step_refusals(lib):
     t.k1_ms = ctypes.pointer(ms)
     assert call(t) == dgd.DGD_EINVAL
     assert "k1_ms" in dgd.dgd_last_error()
+
+
+def test_phase_times_refusals(lib):
+    # the default build records no phase times and says so; bad arguments
+    # are refused first
+    buf = (ctypes.c_uint64 * 16)()
+    assert lib.dgd_phase_times(None, 16) == dgd.DGD_EINVAL
+    assert lib.dgd_phase_times(buf, dgd.PHASE_WORKGROUPS * 4 * dgd.PHASE_SLOTS + 1) == dgd.DGD_EINVAL
+    assert lib.dgd_phase_times(buf, 16) == dgd.DGD_EUNSUPPORTED
+    assert b"DGD_PHASE_TIMING" in lib.dgd_last_error()
+
+
+def test_phase_build_exports_the_same_functions():
+    if not os.path.exists(dgd.LIB_PHASE_PATH):
+        pytest.skip("libdgd_phase.so is not built (__graft_entry__.build() builds it)")
+    phase = ctypes.CDLL(dgd.LIB_PHASE_PATH)
+    for n in declared_functions():
+        assert hasattr(phase, n), n

@@ -13,6 +13,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = [os.path.join(HERE, "csrc", "dgd.hip")]
 OUTPUT = os.path.join(HERE, "libdgd.so")
+# the same library with the projection's phase timing recorded (a measurement
+# build: dgd_phase_times reports only there)
+OUTPUT_PHASE = os.path.join(HERE, "libdgd_phase.so")
 
 HIPCC_FLAGS = [
     "-O3",
@@ -32,18 +35,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    tmp = OUTPUT + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
+def build(verbose: bool = False, phase_timing: bool = False) -> str:
+    out = OUTPUT_PHASE if phase_timing else OUTPUT
+    tmp = out + ".tmp"
+    defs = ["-DDGD_PHASE_TIMING"] if phase_timing else []
+    cmd = [hipcc(), *HIPCC_FLAGS, *defs, "-I", os.path.join(ROOT, "include"), *SOURCES, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libdgd.so")
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
     if verbose:
         sys.stderr.write(res.stderr)
-    os.replace(tmp, OUTPUT)
-    return OUTPUT
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, phase_timing="--phase-timing" in sys.argv))

@@ -59,6 +59,26 @@ constexpr int kThreads = 256;           // merge/commit and init kernels: 4 wave
 #ifndef DGD_EPI_UNROLL
 #define DGD_EPI_UNROLL 4
 #endif
+
+// Phase timing (a measurement build, DGD_PHASE_TIMING defined): the packed
+// projection records, per workgroup (0..1023) and wave, the 100 MHz wall
+// clock at kernel start, at the start, K-loop end and epilogue end of its
+// first four tiles, and at kernel end, plus the shader clock at start and
+// end.  Lane 0 of each wave writes its slots with vector stores; the last
+// launch overwrites the previous one.  dgd_phase_times() reads them.
+constexpr int kPhaseWorkgroups = 1024, kPhaseSlots = 16;
+#ifdef DGD_PHASE_TIMING
+__device__ unsigned long long g_phase[kPhaseWorkgroups * 4 * kPhaseSlots];
+#define PHASE_AT(slot, clk)                                                                    \
+  do {                                                                                         \
+    if ((threadIdx.x & 63) == 0 && blockIdx.x < kPhaseWorkgroups)                              \
+      g_phase[(blockIdx.x * 4 + ((threadIdx.x >> 6) & 3)) * kPhaseSlots + (slot)] = (clk);     \
+  } while (0)
+#else
+#define PHASE_AT(slot, clk) \
+  do {                      \
+  } while (0)
+#endif
 constexpr int kWaves = kThreads / 64;
 constexpr int kPThreads = 512;          // projection: 8 waves, two per SIMD
 constexpr int kVGroups = 4;             // projection waves along the vocabulary ...
@@ -778,6 +798,9 @@ k_project_packed(const ProjArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wv = wave & 3, wp = wave >> 2;
   const int lane = tid & 63, half = lane >> 5, col = lane & 31;
+  PHASE_AT(0, wall_clock64());
+  PHASE_AT(1, clock64());
+  int phase_tile = 0;
 
   int mt, g;
   tile_of_block(blockIdx.x, a.n_mtiles, a.P, mt, g);
@@ -856,6 +879,7 @@ k_project_packed(const ProjArgs a) {
   for (int vt = g; vt < a.n_vtiles; vt += a.P) {
     const int vbase = vt * kVocabTile + wv * kVocabPerWave;
     const __amdgpu_buffer_rsrc_t wr = wres_of(vt);
+    if (phase_tile < 4) PHASE_AT(2 + 3 * phase_tile, wall_clock64());
 
     f32x16_t acc[kVB][NBW];
     auto zero_acc = [&]() {
@@ -1065,6 +1089,7 @@ k_project_packed(const ProjArgs a) {
 
     }
 
+    if (phase_tile < 4) PHASE_AT(3 + 3 * phase_tile, wall_clock64());
     // ---------------- epilogue: one position per lane per block ----------
     // One loop body for EU blocks at a time (the body is long, so the loop
     // is not unrolled further).  Body block u is always taken from acc[.][u]
@@ -1118,6 +1143,8 @@ k_project_packed(const ProjArgs a) {
 #pragma unroll
         for (int k = 0; k + EU < NBW; ++k) acc[vb][k] = acc[vb][k + EU];
     }
+    if (phase_tile < 4) PHASE_AT(4 + 3 * phase_tile, wall_clock64());
+    ++phase_tile;
   }
 
   // ------- merge the four vocabulary waves of each position (fixed order) -------
@@ -1130,6 +1157,8 @@ k_project_packed(const ProjArgs a) {
     const int row = row0 + t;
     if (row < a.M) rec_store(a.part + (size_t)row * a.P + g, r);
   }
+  PHASE_AT(14, wall_clock64());
+  PHASE_AT(15, clock64());
   // ------- self-conditioning candidates: the four band lists of each position -------
   if constexpr (kTopK) {
     for (int t = tid; t < MROWS * kScCand; t += THREADS) {
@@ -2550,6 +2579,20 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
 extern "C" {
 
 const char* dgd_last_error(void) { return g_err.c_str(); }
+
+int dgd_phase_times(uint64_t* dst, size_t n) {
+  g_err.clear();
+  if (!dst) return fail(DGD_EINVAL, "dst is NULL");
+  if (n > (size_t)kPhaseWorkgroups * 4 * kPhaseSlots)
+    return fail(DGD_EINVAL, "n=%zu exceeds %d entries", n, kPhaseWorkgroups * 4 * kPhaseSlots);
+#ifdef DGD_PHASE_TIMING
+  const hipError_t e = hipMemcpyFromSymbol(dst, HIP_SYMBOL(g_phase), n * sizeof(uint64_t));
+  return e == hipSuccess ? DGD_OK : hip_fail(e, "hipMemcpyFromSymbol(phase times)");
+#else
+  return fail(DGD_EUNSUPPORTED, "phase timing is recorded only by a library built with "
+                                "DGD_PHASE_TIMING (build.py --phase-timing)");
+#endif
+}
 
 size_t dgd_state_bytes(int32_t B, int32_t L) {
   if (B < 1 || L < 1) return 0;

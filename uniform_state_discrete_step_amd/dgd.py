@@ -14,6 +14,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdgd.so")
+# the measurement build that records the projection's phase times
+LIB_PHASE_PATH = os.path.join(_HERE, "libdgd_phase.so")
+PHASE_WORKGROUPS, PHASE_SLOTS = 1024, 16
 
 DGD_OK = 0
 DGD_EINVAL = -1
@@ -34,7 +37,7 @@ EXPORTED = ("dgd_state_bytes", "dgd_workspace_bytes", "dgd_init_block", "dgd_ste
             "dgd_packed_vocab_bytes", "dgd_pack_vocab", "dgd_q4_vocab_bytes", "dgd_pack_vocab_q4",
             "dgd_sc_embed", "dgd_label_probs",
             "dgd_ceiling_hbm_read", "dgd_ceiling_mfma_bf16", "dgd_debug_philox",
-            "dgd_debug_gumbel",
+            "dgd_debug_gumbel", "dgd_phase_times",
             "dgd_last_error")
 
 
@@ -153,6 +156,8 @@ def load_library(path: str = LIB_PATH):
     lib.dgd_debug_gumbel.restype = ctypes.c_int
     lib.dgd_debug_gumbel.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
                                      ctypes.c_void_p]
+    lib.dgd_phase_times.restype = ctypes.c_int
+    lib.dgd_phase_times.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
     _lib = lib
     return lib
 
@@ -430,3 +435,12 @@ def dgd_debug_philox(ctr, key, uniform_key: int, out, stream=None):
 def dgd_debug_gumbel(words, out, stream=None):
     _check(load_library().dgd_debug_gumbel(_ptr(words, 4), _ptr(out, 4), int(words.numel()),
                                            _stream_handle(stream)))
+
+
+def dgd_phase_times():
+    """Phase times of the last packed projection (a library built with
+    phase timing only): uint64 array [workgroup, wave, slot]."""
+    import numpy as np
+    out = np.zeros(PHASE_WORKGROUPS * 4 * PHASE_SLOTS, dtype=np.uint64)
+    _check(load_library().dgd_phase_times(out.ctypes.data_as(ctypes.c_void_p), out.size))
+    return out.reshape(PHASE_WORKGROUPS, 4, PHASE_SLOTS)
