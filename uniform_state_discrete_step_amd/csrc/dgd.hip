@@ -717,7 +717,11 @@ __device__ __forceinline__ uint32_t q4_pair(uint32_t codes, int e, float sc, flo
   // even elements in the low nibble of each byte, odd ones in the high: split
   // once into two byte vectors (shared by the four words of a fragment) and
   // convert byte e of each
-  const uint32_t lo = codes & 0x0F0F0F0Fu, hi = (codes >> 4) & 0x0F0F0F0Fu;
+  uint32_t lo = codes & 0x0F0F0F0Fu, hi = (codes >> 4) & 0x0F0F0F0Fu;
+  // opaque to the combiner, so the byte conversions stay v_cvt_f32_ubyteN of
+  // the split words (the same asm on the same code word merges across the
+  // four calls) instead of a bit-field extract each
+  asm("" : "+v"(lo), "+v"(hi));
   const float q0 = (float)((lo >> (8 * e)) & 0xFFu);
   const float q1 = (float)((hi >> (8 * e)) & 0xFFu);
   const float w0 = fmaf(sc, q0, mn), w1 = fmaf(sc, q1, mn);
@@ -929,11 +933,6 @@ k_project_packed(const ProjArgs a) {
         const uint32_t wbase = (uint32_t)(c + RING) * kQ4ChunkBytes;
         const int h2 = c + HB < nkr ? c + HB : c + HB - nkr;
         const int hc2 = h2 < nk ? h2 : 0;
-        auto mfma2 = [&](int s, int pb) {
-          const bf16x8_t a0 = as_bf16x8(abuf[s & 1][0]), a1 = as_bf16x8(abuf[s & 1][1]);
-          acc[0][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, bfr[pb], acc[0][pb], 0, 0, 0);
-          acc[1][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, bfr[pb], acc[1][pb], 0, 0, 0);
-        };
         // the A word (pb) of the step after s: this chunk's codes, or the next
         // chunk's step 0 during step 3
         auto deq_next = [&](int s, int pb) {
@@ -941,25 +940,44 @@ k_project_packed(const ProjArgs a) {
           if (s < 3) deq_word(qcur, scur, s + 1, pb, abuf[(s + 1) & 1]);
           else deq_word(qnext, snext, 0, pb, abuf[0]);
         };
+        // One MFMA, the dequantized word(s) owed after this fragment pair,
+        // the other MFMA, then the LDS read into the B register both have
+        // issued from: the VALU work fills the matrix pipe's time of the
+        // first MFMA as well (a wave waits at the issue of the second until
+        // the pipe takes it).
+        auto mfma1 = [&](int s, int pb, int f) {
+          const bf16x8_t af = as_bf16x8(abuf[s & 1][f]);
+          acc[f][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bfr[pb], acc[f][pb], 0, 0, 0);
+        };
+        auto deq_owed = [&](int s, int pb) {
+          deq_next(s, pb);
+          if constexpr (NBW < 8)
+            if (pb == NBW - 1)
+#pragma unroll
+              for (int k = NBW; k < 8; ++k) deq_next(s, k);
+        };
 #pragma unroll
         for (int s = 0; s < 3; ++s) {
 #pragma unroll
           for (int pb = 0; pb < NBW; ++pb) {
             __builtin_amdgcn_sched_barrier(0);
-            mfma2(s, pb);
+            mfma1(s, pb, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            deq_owed(s, pb);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma1(s, pb, 1);
             __builtin_amdgcn_sched_barrier(0);
             bfr[pb] = read_b(hcur, s + 1, pb);
-            deq_next(s, pb);
-            if constexpr (NBW < 8)
-              if (pb == NBW - 1)
-#pragma unroll
-                for (int k = NBW; k < 8; ++k) deq_next(s, k);
           }
         }
 #pragma unroll
         for (int pb = 0; pb < NBW / 2; ++pb) {
           __builtin_amdgcn_sched_barrier(0);
-          mfma2(3, pb);
+          mfma1(3, pb, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          deq_owed(3, pb);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma1(3, pb, 1);
         }
         __builtin_amdgcn_sched_barrier(0);
         __builtin_amdgcn_s_waitcnt(waitcnt_enc(kDmaLag, 0));
@@ -972,14 +990,14 @@ k_project_packed(const ProjArgs a) {
 #pragma unroll
         for (int pb = NBW / 2; pb < NBW; ++pb) {
           __builtin_amdgcn_sched_barrier(0);
-          mfma2(3, pb);
+          mfma1(3, pb, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          deq_owed(3, pb);
+          __builtin_amdgcn_sched_barrier(0);
+          mfma1(3, pb, 1);
           __builtin_amdgcn_sched_barrier(0);
           bfr[pb] = read_b(hnext, 0, pb);
         }
-        // the next chunk's step-0 words, then the loads of chunk c + RING
-        // into the registers this chunk has finished with
-#pragma unroll
-        for (int k = 0; k < 8; ++k) deq_next(3, k);
         __builtin_amdgcn_sched_barrier(0);
         qcur[0] = __builtin_amdgcn_raw_buffer_load_b128(wr, (wbase + lane_off) | woob, 0, kNonTemporal);
         __builtin_amdgcn_sched_barrier(0);

@@ -9,10 +9,10 @@ kernel's instruction stream is the same as the product build's apart from
 those clock reads and stores.
 
 Usage: ``python -m uniform_state_discrete_step_amd.phase_timing
-[--workload gemma_vocab] [--warmup 12] [--samples 3]``.  Prints, per sampled
-step, the launch's span, its HIP-event time and shader clock, and per tile
-slot the mean start offset, K-loop time and epilogue time over all waves
-(5th and 95th percentiles in brackets), then one JSON line.
+[--workload gemma_vocab] [--layout packed|q4] [--warmup 12] [--samples 3]``.
+Prints, per sampled step, the launch's span, its HIP-event time and shader
+clock, and per tile slot the mean start offset, K-loop time and epilogue time
+over all waves (5th and 95th percentiles in brackets), then one JSON line.
 """
 from __future__ import annotations
 
@@ -58,6 +58,9 @@ def summarize(prev: np.ndarray, cur: np.ndarray) -> dict:
 def main(argv=None) -> None:
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--workload", default="gemma_vocab")
+    ap.add_argument("--layout", choices=("packed", "q4"), default="packed",
+                    help="the bf16 packed table, or the 4-bit table (the synthetic table quantized "
+                         "in groups of 32)")
     ap.add_argument("--warmup", type=int, default=12, help="steps before the sampled ones")
     ap.add_argument("--samples", type=int, default=3, help="sampled steps")
     args = ap.parse_args(argv)
@@ -65,7 +68,7 @@ def main(argv=None) -> None:
     import torch
 
     from uniform_state_discrete_step_amd import dgd
-    from uniform_state_discrete_step_amd.inputs import WORKLOADS, make_workload_arrays
+    from uniform_state_discrete_step_amd.inputs import WORKLOADS, make_workload_arrays, quantize_q4
 
     dgd.load_library(dgd.LIB_PHASE_PATH)   # before anything loads the product build
     wl = WORKLOADS[args.workload]
@@ -73,10 +76,18 @@ def main(argv=None) -> None:
         sys.exit(f"--warmup + --samples must not exceed the {wl.N} steps of a block")
     dev = torch.device("cuda:0")
     W, Hs = make_workload_arrays(wl, threads=16)
-    Wd = dgd.pack_vocab(torch.from_numpy(W.view(np.int16)).to(dev), wl.V, wl.d)
+    if args.layout == "q4":
+        codes, sc, mn = quantize_q4(W)
+        Wd = dgd.pack_vocab_q4(torch.from_numpy(codes.reshape(-1)).to(dev),
+                               torch.from_numpy(sc.reshape(-1).view(np.int16)).to(dev),
+                               torch.from_numpy(mn.reshape(-1).view(np.int16)).to(dev), wl.V, wl.d)
+        layout = dgd.DGD_VOCAB_Q4
+    else:
+        Wd = dgd.pack_vocab(torch.from_numpy(W.view(np.int16)).to(dev), wl.V, wl.d)
+        layout = dgd.DGD_VOCAB_PACKED
     Hd = torch.from_numpy(Hs.view(np.int16)).to(dev)
     ctx = dgd.Context(wl.B, wl.L, wl.V, wl.d, wl.G, wl.bounds, device=dev, outputs=False,
-                      vocab_layout=dgd.DGD_VOCAB_PACKED)
+                      vocab_layout=layout)
     params = dgd.make_params(wl.N, wl.t_min, wl.t_max, wl.confidence, wl.stability_threshold,
                              wl.freeze, wl.final_emit)
     canvas = torch.zeros(wl.B * wl.G, dtype=torch.int32, device=dev)
@@ -109,7 +120,7 @@ def main(argv=None) -> None:
                   f"[{tl['epilogue_p5_p95'][0]:5.1f}, {tl['epilogue_p5_p95'][1]:5.1f}]", flush=True)
         print(f"  prologue {r['prologue_us']:.1f} us, final merge {r['final_merge_us']:.1f} us",
               flush=True)
-    print(json.dumps({"workload": wl.name, "samples": results}))
+    print(json.dumps({"workload": wl.name, "layout": args.layout, "samples": results}))
 
 
 if __name__ == "__main__":
