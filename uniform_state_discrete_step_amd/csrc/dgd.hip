@@ -55,9 +55,13 @@ constexpr int kThreads = 256;           // merge/commit and init kernels: 4 wave
 // Blocks of 32 positions per epilogue loop body of the packed projection
 // (four: the accumulator rotation between bodies then moves 256 instead of
 // 1792 registers per tile, 14 us less at 256 x 262144 x 2816; the variant
-// that also keeps top-K lists runs out of registers with four and uses one)
+// that also keeps top-K lists runs out of registers with four and uses two,
+// 6 us less than one)
 #ifndef DGD_EPI_UNROLL
 #define DGD_EPI_UNROLL 4
+#endif
+#ifndef DGD_EPI_UNROLL_TOPK
+#define DGD_EPI_UNROLL_TOPK 2
 #endif
 
 // Phase timing (a measurement build, DGD_PHASE_TIMING defined): the packed
@@ -1114,7 +1118,7 @@ k_project_packed(const ProjArgs a) {
     // and the accumulators are rotated down EU blocks at the end of the body,
     // so every register index stays static and the accumulators never leave
     // AGPRs.
-    constexpr int EU0 = kTopK ? 1 : DGD_EPI_UNROLL;
+    constexpr int EU0 = kTopK ? DGD_EPI_UNROLL_TOPK : DGD_EPI_UNROLL;
     constexpr int EU = NBW < EU0 ? NBW : EU0;
     static_assert(NBW % EU == 0, "epilogue unroll");
 #pragma unroll 1
