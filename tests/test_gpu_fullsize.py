@@ -9,7 +9,10 @@ row-major table.
   logits are checked on one row of every 32-position MFMA block.
 * The other full-size runs compare per-position statistics (entropy,
   argmax, sample, gap) on one row of every 32-position block of every canvas
-  at sampled steps, recomputed by the oracle for those rows, and the whole
+  at sampled steps, and on every position of every canvas at every fourth
+  step of every block (the batched and multi-block workloads) or at two
+  steps (the variants of the headline run), recomputed by the oracle for
+  those rows, and the whole
   step's decision logic (early stop, sort, entropy bound, sample write,
   re-noise) at EVERY step: the oracle's step rule applied to the GPU's own
   per-position statistics must reproduce the GPU's new canvas, committed
@@ -106,8 +109,9 @@ class FullRun:
             sv["prev_argmax"][c * wl.L:(c + 1) * wl.L].cpu().numpy().astype(np.int64),
             int(sv["stable_count"][c]), bool(int(sv["done"][c])), int(sv["steps_used"][c]))
 
-    def sampled_rows(self, rep, b, s):
-        """Statistics of one row in every 32-position block of every canvas."""
+    def sampled_rows(self, rep, b, s, every_row=False):
+        """Statistics of one row in every 32-position block of every canvas
+        (of every row, with every_row)."""
         wl = self.wl
         if self.W64 is None:
             self.W64 = O.bf16_to_f64(self.W)
@@ -118,7 +122,7 @@ class FullRun:
         Tk = self.ctx.token.cpu().numpy().astype(np.int64)
         gap = self.ctx.gap.cpu().numpy()
         for c in range(wl.B):
-            rows = block_rows(wl.L, rng)
+            rows = np.arange(wl.L) if every_row else block_rows(wl.L, rng)
             z = O.logits(self.Hs[b, s, c][rows], self.W, self.tail, W64=self.W64)
             p_abs, gstep = b * wl.L + rows, b * wl.N + s
             st = oracle_stats(z, T, wl.seeds[c], p_abs, gstep)
@@ -152,7 +156,7 @@ class FullRun:
             rep.fail(f"{tag}: convergence band flag {int(sv['band_conv'][c])} "
                      f"(|mean - confidence| = {dconf:.3e})")
 
-    def run(self, sample_every=8, blocks=None):
+    def run(self, sample_every=8, blocks=None, full_steps=()):
         torch, wl, dgd = self.torch, self.wl, self.dgd
         rep = Report()
         for b in (range(wl.blocks) if blocks is None else blocks):
@@ -192,7 +196,10 @@ class FullRun:
                         self.check_band_counters(rep, tag, c, info, gap[sl])
                     rep.steps += 1
                     rep.positions += wl.L
-                if s % sample_every == 0 or s == wl.N - 1:
+                if s in full_steps:
+                    self.sampled_rows(rep, b, s, every_row=True)
+                    progress(f"{wl.name} block {b} step {s} (every position): {rep.summary()}")
+                elif s % sample_every == 0 or s == wl.N - 1:
                     self.sampled_rows(rep, b, s)
                     progress(f"{wl.name} block {b} step {s}: {rep.summary()}")
                 if all(self.gpu_state(c).done for c in range(wl.B)):
@@ -262,7 +269,7 @@ def test_batched_full_run_and_batch_invariance(dev):
     import torch
     wl = WORKLOADS["batched"]
     run = FullRun(wl, dev)
-    _check(run.run(sample_every=6), wl.name)
+    _check(run.run(sample_every=6, full_steps=range(0, wl.N, 4)), wl.name)
     # canvas 5 of the batch, run alone, must be bitwise identical
     c = 5
     alone = shrink(wl, name="batched_c5", B=1, seeds=(wl.seeds[c],), bounds=(wl.bounds[c],))
@@ -282,14 +289,14 @@ def test_gemma_vocab_full_run_with_lm_head_tail(dev):
     from uniform_state_discrete_step_amd.inputs import make_norm_weight
     wl = WORKLOADS["gemma_vocab"]
     tail = O.Tail(norm_weight=make_norm_weight(wl.d, wl.cfg_seed), norm_eps=1e-6, softcap=30.0)
-    _check(FullRun(wl, dev, tail=tail).run(sample_every=6),
+    _check(FullRun(wl, dev, tail=tail).run(sample_every=6, full_steps=(0, 24)),
            f"{wl.name} with output norm and softcap")
 
 
 def test_gemma_vocab_full_run_q4_table(dev):
     """The 4-bit table stream at the full size."""
     wl = WORKLOADS["gemma_vocab"]
-    _check(FullRun(wl, dev, layout=2).run(sample_every=6),
+    _check(FullRun(wl, dev, layout=2).run(sample_every=6, full_steps=(0, 24)),
            f"{wl.name} 4-bit table")
 
 
@@ -299,7 +306,7 @@ def test_gemma_vocab_full_run_with_self_conditioning(dev):
     wl = WORKLOADS["gemma_vocab"]
     tail = O.Tail(norm_weight=make_norm_weight(wl.d, wl.cfg_seed), norm_eps=1e-6, softcap=30.0)
     run = FullRun(wl, dev, tail=tail, sc_topk=32)
-    rep = run.run(sample_every=8)
+    rep = run.run(sample_every=8, full_steps=(0,))
     st = run.ctx.sc_status.cpu().numpy()
     print(f"\nrecomputed parts in the last step: {int(st.sum())}, rows budget-exhausted "
           f"{int((st < 0).sum())}", flush=True)
@@ -309,7 +316,8 @@ def test_gemma_vocab_full_run_with_self_conditioning(dev):
 @pytest.mark.parametrize("layout", [1, 0], ids=["packed", "rows"])
 def test_multi_block_full_run(dev, layout):
     wl = WORKLOADS["multi_block"]
-    _check(FullRun(wl, dev, layout=layout).run(sample_every=8),
+    full = range(0, wl.N, 4) if layout == 1 else ()
+    _check(FullRun(wl, dev, layout=layout).run(sample_every=8, full_steps=full),
            f"{wl.name} layout={layout}")
 
 
