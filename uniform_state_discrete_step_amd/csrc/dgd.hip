@@ -858,12 +858,14 @@ k_project_packed(const ProjArgs a) {
   const int hseg = (lane & 7) ^ swz((lane >> 3) + 8 * (wave & 1));
   const int last_rel = a.M - 1 - row0;
   const uint32_t d2 = (uint32_t)(d * 2);
-  auto dma_h = [&](int c, uint8_t* hbuf) {
+  // loads i0 .. i1-1 of the chunk's HSEG (all by default)
+  auto dma_h = [&](int c, uint8_t* hbuf, int i0 = 0, int i1 = -1) {
+    if (i1 < 0) i1 = HSEG;
     const uint32_t koff = c * kKChunk + hseg * 8 < a.d ? (uint32_t)(c * kKChunk * 2) : 0u - (uint32_t)hseg * 16;
     const uint32_t lbase =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)hbuf + (uint32_t)wave * 1024u;
 #pragma unroll
-    for (int i = 0; i < HSEG; ++i) {
+    for (int i = i0; i < i1; ++i) {
       const int r = min((i * WAVES + wave) * 8 + (lane >> 3), last_rel);
       const uint32_t off = (uint32_t)r * d2 + (uint32_t)hseg * 16 + koff;
       asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
@@ -990,18 +992,25 @@ k_project_packed(const ProjArgs a) {
 #pragma unroll
         for (int pb = 0; pb < NBW / 2; ++pb) bfr[pb] = read_b(hnext, 0, pb);
         __builtin_amdgcn_sched_barrier(0);
-        dma_h(hc2, hcur);
+        // the DMA of H(c+HB) spread over the MFMA windows of the second half
+        {
+          constexpr int NH = NBW - NBW / 2, PER = (HSEG + 2 * NH - 1) / (2 * NH);
 #pragma unroll
-        for (int pb = NBW / 2; pb < NBW; ++pb) {
-          __builtin_amdgcn_sched_barrier(0);
-          mfma1(3, pb, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          deq_owed(3, pb);
-          __builtin_amdgcn_sched_barrier(0);
-          mfma1(3, pb, 1);
-          __builtin_amdgcn_sched_barrier(0);
-          bfr[pb] = read_b(hnext, 0, pb);
+          for (int j = 0; j < NH; ++j) {
+            const int pb = NBW / 2 + j;
+            __builtin_amdgcn_sched_barrier(0);
+            mfma1(3, pb, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            dma_h(hc2, hcur, min(HSEG, 2 * j * PER), min(HSEG, (2 * j + 1) * PER));
+            deq_owed(3, pb);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma1(3, pb, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            dma_h(hc2, hcur, min(HSEG, (2 * j + 1) * PER), min(HSEG, (2 * j + 2) * PER));
+            bfr[pb] = read_b(hnext, 0, pb);
+          }
         }
+
         __builtin_amdgcn_sched_barrier(0);
         qcur[0] = __builtin_amdgcn_raw_buffer_load_b128(wr, (wbase + lane_off) | woob, 0, kNonTemporal);
         __builtin_amdgcn_sched_barrier(0);
@@ -1045,9 +1054,12 @@ k_project_packed(const ProjArgs a) {
       // the W registers of step s.  Step 3 is split around the chunk's only
       // barrier: the first half of its MFMAs, a wait for this wave's DMA of
       // H(c+1) (kDmaLag later loads may stay in flight) and for its LDS reads,
-      // the barrier, then the reads of step 0 of chunk c+1 from hnext and the
-      // DMA of H(c+HB) into hcur (every wave has read its last fragment of
-      // chunk c before the barrier), then the rest.
+      // the barrier, then the reads of step 0 of chunk c+1 from hnext for the
+      // first half, then the rest of the MFMAs with the DMA of H(c+HB) into
+      // hcur spread over their issue windows, one or two loads after each
+      // MFMA (every wave has read its last fragment of chunk c before the
+      // barrier; the DMA loads are still all issued before the step's W
+      // loads, so the count kDmaLag is unchanged).
       auto chunk = [&](int c, u32x4_t (&wreg)[8], uint8_t* hcur, const uint8_t* hnext) {
         const uint32_t woob = (uint32_t)(c + RING >= nk) << 31;
         const uint32_t wbase = (uint32_t)(c + RING) * kPackChunkBytes + lane_off;
@@ -1088,14 +1100,28 @@ k_project_packed(const ProjArgs a) {
 #pragma unroll
         for (int pb = 0; pb < NBW / 2; ++pb) bfr[pb] = read_b(hnext, 0, pb);
         __builtin_amdgcn_sched_barrier(0);
-        dma_h(hc2, hcur);
+        // the DMA of H(c+HB) spread over the MFMA windows of the second half
+        {
+          auto mfma1 = [&](int pb, int f) {
+            acc[f][pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(wreg[6 + f]), bfr[pb], acc[f][pb],
+                                                                 0, 0, 0);
+          };
+          constexpr int NH = NBW - NBW / 2, PER = (HSEG + 2 * NH - 1) / (2 * NH);
 #pragma unroll
-        for (int pb = NBW / 2; pb < NBW; ++pb) {
-          __builtin_amdgcn_sched_barrier(0);
-          mfma2(3, pb);
-          __builtin_amdgcn_sched_barrier(0);
-          bfr[pb] = read_b(hnext, 0, pb);
+          for (int j = 0; j < NH; ++j) {
+            const int pb = NBW / 2 + j;
+            __builtin_amdgcn_sched_barrier(0);
+            mfma1(pb, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            dma_h(hc2, hcur, min(HSEG, 2 * j * PER), min(HSEG, (2 * j + 1) * PER));
+            __builtin_amdgcn_sched_barrier(0);
+            mfma1(pb, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            dma_h(hc2, hcur, min(HSEG, (2 * j + 1) * PER), min(HSEG, (2 * j + 2) * PER));
+            bfr[pb] = read_b(hnext, 0, pb);
+          }
         }
+
         __builtin_amdgcn_sched_barrier(0);
         wload(3);
         __builtin_amdgcn_sched_barrier(0);
