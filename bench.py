@@ -7,6 +7,7 @@ resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload gemma_vocab]
                     [--no-cpu-baseline] [--profile-only] [--lm-head-tail] [--sc-topk K]
+                    [--power-seconds S]
     python bench.py --oracle-timing      # the CPU oracle on every workload, no GPU
 
 ``--lm-head-tail`` adds the model's output norm before the projection and the
@@ -18,6 +19,10 @@ no Python runs between steps.  Before them: the measured HBM and MFMA
 ceilings, then one instrumented pass of the whole generation with HIP events
 around every kernel of every step (the projection's average launch for
 ``roofline``, and the per-step split), then the W warmup steps.
+
+After them, ``power`` runs the step for ``--power-seconds`` more while
+sampling the socket power and graphics clocks with amd-smi (outside the timed
+region).
 
 Prints ONE JSON line.  ``roofline`` is for the dominant kernel (the fused
 projection); ``cpu_baseline`` times the CPU oracle on a bounded sample of the
@@ -92,6 +97,39 @@ def measured_ceilings(dgd, torch, table, dev):
     return {"hbm_read_GBs": hbm, "mfma_bf16_TFLOPs": mfma,
             "how": "streaming 16-byte reads of the step's table (best of 5); "
                    "v_mfma_f32_32x32x16_bf16 on operands from the table, one wave per SIMD (best of 5)"}
+
+
+def power_leg(run_steps, torch, seconds, start):
+    """Sustained step rate with the socket power and graphics clocks sampled
+    meanwhile (outside the timed region).  The board holds its socket power at
+    a cap by lowering the clocks, so at the cap the step's energy sets its
+    time."""
+    from uniform_state_discrete_step_amd.power_trace import Sampler, power_cap
+
+    smp = Sampler(0.5)
+    smp.start()
+    i, batch = start, 48
+    run_steps(batch, start=i)     # let the sampler and the clocks settle
+    torch.cuda.synchronize()
+    i += batch
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        run_steps(batch, start=i)
+        torch.cuda.synchronize()
+        i += batch
+        n += batch
+    t1 = time.perf_counter()
+    r = smp.between(t0, t1)
+    smp.stop.set()
+    smp.join()
+    rate = n / (t1 - t0)
+    cap = power_cap()
+    r.update({"steps_per_s": rate, "power_cap_W": float(cap) if cap else None,
+              "mJ_per_step": (r["socket_power_W"] / rate * 1e3) if r["socket_power_W"] else None,
+              "how": f"{n} steps back to back over {t1 - t0:.1f} s after the timed loop; "
+                     "amd-smi metric --power --clock every 0.5 s (median; first sample skipped)"})
+    return r
 
 
 def cpu_model_name():
@@ -187,6 +225,9 @@ def main():
                     help="also time the sparse label read (dgd_label_probs) of this many labels "
                          "over the workload's positions")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--power-seconds", type=float, default=3.0,
+                    help="after the timed loop, run the step this long while sampling socket "
+                         "power and graphics clocks (amd-smi); 0 skips it")
     ap.add_argument("--profile-only", action="store_true",
                     help="only the timed loop (for rocprofv3 runs)")
     ap.add_argument("--oracle-timing", action="store_true",
@@ -386,6 +427,8 @@ def main():
             "other": ms / args.steps * 1e3 - (k1_avg_s + tail_avg_s) * 1e6},
         "roofline": roof,
     }
+    if args.power_seconds > 0:
+        out["power"] = power_leg(run_steps, torch, args.power_seconds, args.warmup + args.steps)
     if args.label_read:
         n = args.label_read
         labels = [int(v) for v in np.linspace(0, wl.V - 1, n).astype(np.int64)]
