@@ -244,25 +244,29 @@ __device__ __forceinline__ float softcap_bits(float z, float cin, float cout) {
 // z[vb][4q + e] (lane half h) is the logit of id vbase + 32 vb + 8 q + 4 h + e.
 // The two halves' records are merged; both lanes return the merged record.
 // kCap: the logits pass through the softcap first (c2 is then unused).
-template <bool kUniformKey, bool kCap>
+// kInPlace: z is left holding the tempered logits in bits (the top-K lists
+// read them); otherwise z keeps the raw logits and the scale by c2 is fused
+// into the operations that use it (one rounding instead of two).
+template <bool kUniformKey, bool kCap, bool kInPlace>
 __device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int half, int V, float c2,
                                            float cin, float cout, uint32_t pabs, uint32_t gstep,
                                            uint32_t key0, uint32_t key1) {
-  // Tempered logits in bits, x2 = z * c2, computed once in place (a plain,
-  // non-contracted multiply).  value index i = vb*16 + 4q + e  <->
-  // vocabulary id vbase + vb*32 + 8q + 4h + e.  In a ragged last tile, ids
-  // past V get kMasked, far below the running-max start kNeg: they add exact
-  // zeros to S and A and never win the argmax or the sample.
+  static_assert(!kCap || kInPlace, "the capped logits are computed in place");
+  // value index i = vb*16 + 4q + e  <->  vocabulary id vbase + vb*32 + 8q + 4h + e
   if constexpr (kCap) {
 #pragma unroll
     for (int i = 0; i < kVB * 16; ++i) {
       z[i >> 4][i & 15] = softcap_bits(z[i >> 4][i & 15], cin, cout);
       if ((i & 15) == 15) __builtin_amdgcn_sched_barrier(0);
     }
-  } else {
+  } else if constexpr (kInPlace) {
 #pragma unroll
     for (int i = 0; i < kVB * 16; ++i) z[i >> 4][i & 15] = __fmul_rn(z[i >> 4][i & 15], c2);
   }
+  const float sc = kInPlace ? 1.f : c2;   // from the values in z to bits
+  // In a ragged last tile, ids past V get kMasked (raw or in bits: c2 > 1
+  // keeps it below kNeg either way): they add exact zeros to S and A and
+  // never win the argmax or the sample.
   if (vbase + kVocabPerWave > V) {
 #pragma unroll
     for (int i = 0; i < kVB * 16; ++i) {
@@ -270,30 +274,30 @@ __device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int ha
       z[i >> 4][i & 15] = v < V ? z[i >> 4][i & 15] : kMasked;
     }
   }
-  float m = kNeg;
-  int am = kNoIndex;
+  auto off = [](int i) { return (i >> 4) * 32 + 8 * ((i >> 2) & 3) + (i & 3); };
+  // Largest value (max3 chains); its tempered value round(mr * sc) is the
+  // largest tempered logit, rounding being monotone.
+  float mr = kNeg;
 #pragma unroll
-  for (int i = 0; i < kVB * 16; ++i) {   // first maximum (ids increase with i)
-    const int v = vbase + (i >> 4) * 32 + 8 * ((i >> 2) & 3) + 4 * half + (i & 3);
-    const float x = z[i >> 4][i & 15];
-    am = x > m ? v : am;
-    m = fmaxf(m, x);
-  }
-  // Scheduling barriers bound how far the scheduler may hoist work across
-  // the value loops: unbounded, it keeps every intermediate of the block
-  // live at once and spills.
+  for (int i = 0; i < kVB * 16; ++i) mr = fmaxf(mr, z[i >> 4][i & 15]);
+  const float m = fmaxf(__fmul_rn(mr, sc), kNeg);
   __builtin_amdgcn_sched_barrier(0);
+  // Sums and the first index of the maximum, last value first (so the
+  // final assignment is the smallest id).
   float S = 0.f, A = 0.f;
+  int ao = -1;
 #pragma unroll
-  for (int i = 0; i < kVB * 16; ++i) {
-    const float dx = z[i >> 4][i & 15] - m;
+  for (int i = kVB * 16 - 1; i >= 0; --i) {
+    const float zi = z[i >> 4][i & 15];
+    const float dx = fmaf(zi, sc, -m);
     const float e = fexp2(dx);
     S += e;
     A = fmaf(dx, e, A);
-    if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+    ao = zi == mr ? off(i) : ao;
+    if ((i & 7) == 0) __builtin_amdgcn_sched_barrier(0);
   }
   float y1 = kNeg, y2 = kNeg;
-  int i1 = kNoIndex;
+  int io = -1;
 #pragma unroll
   for (int grp = 0; grp < kVB * 4; ++grp) {
     const int v0 = vbase + (grp >> 2) * 32 + 8 * (grp & 3) + 4 * half;
@@ -306,16 +310,18 @@ __device__ __forceinline__ Rec tile_record(f32x16_t (&z)[kVB], int vbase, int ha
 #pragma unroll
     for (int e = 0; e < 4; ++e) {   // top two, first index on ties
       const int i = 4 * grp + e;
-      const float y = z[i >> 4][i & 15] + gumbel_bits(words[e]);
-      y2 = fmaxf(y2, fminf(y, y1));
-      i1 = y > y1 ? v0 + e : i1;
-      y1 = fmaxf(y1, y);
+      const float y = fmaf(z[i >> 4][i & 15], sc, gumbel_bits(words[e]));
+      y2 = __builtin_amdgcn_fmed3f(y, y1, y2);   // y2 <= y1: max(y2, min(y, y1))
+      const bool gt = y > y1;
+      io = gt ? off(i) : io;
+      y1 = gt ? y : y1;
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  const int vlane = vbase + 4 * half;
   Rec loc;
-  loc.m = m; loc.S = S; loc.A = A; loc.am = am;
-  loc.y1 = y1; loc.i1 = i1; loc.y2 = y2; loc.pad = 0.f;
+  loc.m = m; loc.S = S; loc.A = A; loc.am = ao < 0 ? kNoIndex : vlane + ao;
+  loc.y1 = y1; loc.i1 = io < 0 ? kNoIndex : vlane + io; loc.y2 = y2; loc.pad = 0.f;
   const Rec oth = rec_shfl_xor(loc, 32);
   return rec_merge(rec_pick(half == 0, loc, oth), rec_pick(half == 0, oth, loc));
 }
@@ -629,7 +635,7 @@ k_project(const ProjArgs a) {
         }
       }
 
-      const Rec wrec = tile_record<kUniformKey, kCap>(z, vbase, half, a.V, a.c2, a.cap_in, a.cap_out, pabs,
+      const Rec wrec = tile_record<kUniformKey, kCap, kCap>(z, vbase, half, a.V, a.c2, a.cap_in, a.cap_out, pabs,
                                                       (uint32_t)a.gstep, key0, key1);
       if (half == 0) {
         Rec* slot = recs + wave * PPW + pb * 32 + col;
@@ -1177,7 +1183,8 @@ k_project_packed(const ProjArgs a) {
               }
           }
         }
-        const Rec wrec = tile_record<kUniformKey, kCap>(z, vbase, half, a.V, a.c2, a.cap_in, a.cap_out,
+        const Rec wrec = tile_record<kUniformKey, kCap, kCap || kTopK>(z, vbase, half, a.V, a.c2, a.cap_in,
+                                                                       a.cap_out,
                                                         pabs, (uint32_t)a.gstep, key0, key1);
         if (half == 0) {
           Rec* slot = recs + wave * PPW + pb * 32 + col;

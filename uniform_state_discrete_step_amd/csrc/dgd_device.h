@@ -89,9 +89,11 @@ __device__ __forceinline__ int32_t word_to_token(uint32_t w, uint32_t V) {
   return (int32_t)(((uint64_t)w * V) >> 32);
 }
 
-// -log2(-log2 u) with u = ((w >> 9) + 1/2) 2^-23 (exact in fp32).
+// -log2(-log2 u) with u = ((w >> 9) + 1/2) 2^-23 (exact in fp32): the word's
+// top 23 bits under the exponent of 1.0 give 1 + (w >> 9) 2^-23 (one
+// v_alignbit_b32), and subtracting 1 - 2^-24 from it is exact.
 __device__ __forceinline__ float gumbel_bits(uint32_t w) {
-  const float u = ((float)(w >> 9) + 0.5f) * 0x1p-23f;
+  const float u = __uint_as_float(__builtin_amdgcn_alignbit(0x7Fu, w, 9u)) - 0x1.fffffep-1f;
   const float nl = -__builtin_amdgcn_logf(u);      // -log2 u > 0
   return -__builtin_amdgcn_logf(nl);
 }
