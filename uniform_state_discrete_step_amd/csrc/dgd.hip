@@ -55,13 +55,12 @@ constexpr int kThreads = 256;           // merge/commit and init kernels: 4 wave
 // Blocks of 32 positions per epilogue loop body of the packed projection
 // (four: the accumulator rotation between bodies then moves 256 instead of
 // 1792 registers per tile, 14 us less at 256 x 262144 x 2816; the variant
-// that also keeps top-K lists runs out of registers with four and uses two,
-// 6 us less than one)
+// that also keeps top-K lists fits four as well, without spills)
 #ifndef DGD_EPI_UNROLL
 #define DGD_EPI_UNROLL 4
 #endif
 #ifndef DGD_EPI_UNROLL_TOPK
-#define DGD_EPI_UNROLL_TOPK 2
+#define DGD_EPI_UNROLL_TOPK 4
 #endif
 
 // Phase timing (a measurement build, DGD_PHASE_TIMING defined): the packed
@@ -359,12 +358,14 @@ __device__ __forceinline__ void sc_insert(float (&lx)[N], uint32_t (&li)[N], flo
   bool b[N];
 #pragma unroll
   for (int k = 0; k < N; ++k) b[k] = x > lx[k];
+  // values: entry k becomes the median of (x, entry k-1, entry k), the list
+  // being sorted; ids follow the comparisons
 #pragma unroll
   for (int k = N - 1; k >= 1; --k) {
-    lx[k] = b[k - 1] ? lx[k - 1] : (b[k] ? x : lx[k]);
+    lx[k] = __builtin_amdgcn_fmed3f(x, lx[k - 1], lx[k]);
     li[k] = b[k - 1] ? li[k - 1] : (b[k] ? i : li[k]);
   }
-  lx[0] = b[0] ? x : lx[0];
+  lx[0] = fmaxf(lx[0], x);
   li[0] = b[0] ? i : li[0];
 }
 
@@ -388,11 +389,12 @@ __device__ __forceinline__ void sc_tile_update(const f32x16_t (&z)[kVB], int vba
     const float x = z[i >> 4][i & 15];
     const int off = (i >> 4) * 32 + 8 * ((i >> 2) & 3) + (i & 3);
     const bool c0 = x > t0, c1 = x > t1, c2 = x > t2;
-    t2 = c1 ? t1 : (c2 ? x : t2);
+    // t0 >= t1 >= t2: each new value is a median of three (or the maximum)
+    t2 = __builtin_amdgcn_fmed3f(x, t1, t2);
     o2 = c1 ? o1 : (c2 ? off : o2);
-    t1 = c0 ? t0 : (c1 ? x : t1);
+    t1 = __builtin_amdgcn_fmed3f(x, t0, t1);
     o1 = c0 ? o0 : (c1 ? off : o1);
-    t0 = c0 ? x : t0;
+    t0 = fmaxf(t0, x);
     o0 = c0 ? off : o0;
     if ((i & 7) == 7) __builtin_amdgcn_sched_barrier(0);
   }
