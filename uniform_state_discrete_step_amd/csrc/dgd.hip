@@ -126,7 +126,7 @@ struct ProjArgs {
   int32_t P, n_vtiles, n_mtiles;
   int32_t block, gstep;
   float c2;               // log2(e) / T_s
-  float cap_in, cap_out;  // softcap: 1 / c and c * c2 (used only when the cap is on)
+  float cap_in, cap_out;  // softcap: 2 log2(e) / c and c * c2 (used only when the cap is on)
   struct ScEnt* cand;     // [M][P][kScCand] self-conditioning candidates, or null
   uint32_t key[DGD_MAX_CANVASES][2];
 };
@@ -229,14 +229,15 @@ constexpr int waitcnt_enc(int vm, int lgkm) {
 }
 
 // Softcapped logit in bits: c * tanh(z / c) * log2(e) / T, given
-// cin = 1 / c and cout = c * log2(e) / T.  tanh(t) = sign(t) (1 - e) / (1 + e)
-// with e = 2^(-2 log2(e) |t|): absolute error a few 2^-24 (the cancellation in
-// 1 - e near t = 0 is absolute, not relative), then scaled by cout.
+// cin = 2 log2(e) / c and cout = c * log2(e) / T.  tanh(t) = 1 - 2 / (e + 1)
+// with e = 2^(2 log2(e) t) = e^(2t): for large t, e = inf and the result is
+// exactly cout; for very negative t, e = 0 and it is exactly -cout.  Absolute
+// error a few 2^-24 of the tanh (the cancellation in 1 - 2 / (e + 1) near
+// t = 0 is absolute, not relative), then scaled by cout.
 __device__ __forceinline__ float softcap_bits(float z, float cin, float cout) {
-  const float t = z * cin;
-  const float e = fexp2(fabsf(t) * -2.8853900817779268f);
-  const float r = (1.f - e) * __builtin_amdgcn_rcpf(1.f + e);
-  return copysignf(r, t) * cout;
+  const float e = fexp2(z * cin);
+  const float r = __builtin_amdgcn_rcpf(e + 1.f);
+  return fmaf(-2.f * cout, r, cout);
 }
 
 // Record of one position over the 64 vocabulary ids held by a lane pair:
@@ -2543,7 +2544,7 @@ int launch_step(const dgd_bf16* H, const dgd_bf16* W, int32_t* canvas, uint8_t* 
   pa.c2 = (float)(kLog2e / T);
   const bool cap = ctx->softcap != 0.f;
   if (cap) {
-    pa.cap_in = (float)(1.0 / ctx->softcap);
+    pa.cap_in = (float)(2.0 * kLog2e / ctx->softcap);
     pa.cap_out = (float)(ctx->softcap * kLog2e / T);
   }
   fill_keys(pa.key, seed, B);
@@ -2864,7 +2865,7 @@ int dgd_label_probs(const dgd_bf16* H, int32_t rows, const dgd_bf16* W_vocab, in
   la.packed = vocab_layout == DGD_VOCAB_PACKED ? 1 : 0;
   la.c2 = (float)(kLog2e / (double)temperature);
   la.cap = softcap;
-  la.cap_in = softcap != 0.f ? (float)(1.0 / softcap) : 0.f;
+  la.cap_in = softcap != 0.f ? (float)(2.0 * kLog2e / softcap) : 0.f;
   for (int i = 0; i < n_labels; ++i) la.labels[i] = labels[i];
   hipLaunchKernelGGL(k_label, dim3((unsigned)rows), dim3(kThreads), 0, (hipStream_t)stream, la);
   const hipError_t e = hipGetLastError();
