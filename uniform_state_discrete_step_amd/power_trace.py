@@ -23,6 +23,14 @@ import time
 import numpy as np
 
 
+def parse_smi(out: str) -> tuple[float | None, list[float]]:
+    """(socket power in W, graphics clock of each XCD in MHz) from the JSON
+    text of ``amd-smi metric --power --clock --json`` (first GPU)."""
+    p = re.search(r'"socket_power":\s*\{\s*"value":\s*([0-9.]+)', out)
+    clks = re.findall(r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*([0-9.]+)', out)
+    return (float(p.group(1)) if p else None), [float(c) for c in clks]
+
+
 def read_smi() -> tuple[float | None, list[float]]:
     """(socket power in W, graphics clock of each XCD in MHz) of GPU 0."""
     try:
@@ -30,9 +38,7 @@ def read_smi() -> tuple[float | None, list[float]]:
                              capture_output=True, text=True, timeout=10).stdout
     except (OSError, subprocess.TimeoutExpired):
         return None, []
-    p = re.search(r'"socket_power":\s*\{\s*"value":\s*([0-9.]+)', out)
-    clks = re.findall(r'"gfx_\d+":\s*\{\s*"clk":\s*\{\s*"value":\s*([0-9.]+)', out)
-    return (float(p.group(1)) if p else None), [float(c) for c in clks]
+    return parse_smi(out)
 
 
 def power_cap() -> str | None:
