@@ -479,13 +479,16 @@ def test_projection_is_exact_on_small_integers(dev, layout):
 
 # ----------------------------------------------------------------------------
 def test_first_step_from_uniform_logits(dev, layout):
-    """H = 0 gives uniform logits: entropy ln V everywhere and one commit, at position 0."""
+    """H = 0 gives uniform logits: entropy ln V everywhere, every argmax the
+    first id (ties go to the lowest id, across lanes, waves, tiles and
+    vocabulary groups) and one commit, at position 0."""
     wl = shrink(WORKLOADS["tiny"], V=2048, d=64, L=64, G=64, N=4)
     W, _ = make_workload_arrays(wl, threads=1)
     Hs = np.zeros((1, wl.N, 1, wl.L, wl.d), dtype=np.uint16)
     ls, rep = run_lockstep(wl, dev, W=W, Hs=Hs, steps=[0], layout=layout)
     H = ls.ctx.entropy.cpu().numpy()
     assert np.all(np.abs(H - math.log(wl.V)) < 1e-5)
+    assert np.all(ls.ctx.argmax.cpu().numpy() == 0)
     com = ls.committed.cpu().numpy()
     assert com.tolist() == [1] + [0] * (wl.L - 1)
 
