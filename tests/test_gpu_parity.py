@@ -134,6 +134,9 @@ def test_tiny_lockstep(dev, layout):
     dict(stability_threshold=0, confidence=1.0),
     dict(N=1),
     dict(N=3, t_min=0.0, t_max=1.0),
+    # near-greedy temperature on a ragged vocabulary: tempered logits ~1e3x
+    # the raw ones, masked ids far below them, one-hot distributions
+    dict(V=1001, N=2, t_min=0.001, t_max=0.001),
 ])
 def test_tiny_variants(dev, variant, layout):
     run_lockstep(shrink(WORKLOADS["tiny"], **variant), dev, layout=layout)
